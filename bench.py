@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of libtgemm's fp32 C = A·B on one MI355X; prints one JSON line.
+
+A step is one call of the product (tgemm_sgemm) on seeded synthetic inputs
+that are already resident in device memory.  Default workload: 8192³ with
+U[-1,1] inputs (seed 4); the 4096³ workload (seed 2) is timed the same way
+and reported alongside, since the headline metric covers both sizes.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+                  [--kernel auto|naive|lds16|lds32|mfma:<variant>]
+                  [--also NAME,...] [--no-cpu-baseline]
+
+Reported:
+* value / ms_per_step — wall clock over the timed steps, between two device
+  synchronisations, throughput = 2·M·N·K / time;
+* roofline — the product kernel's average duration from HIP events recorded
+  on the stream it is launched on, its algorithmic flops (2·M·N·K per
+  launch) over that time, against the MI355X dense fp32 matrix peak; the
+  measured HBM traffic per launch comes from the committed rocprofv3 counter
+  summary when it was taken on the current kernel source, else null;
+* cpu_baseline — the CPU oracle (float64, test infrastructure) timed on this
+  host's cores on a bounded sample: whole rows of the same product.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp32 GEMM TFLOPS + % of MI355X FP32 matrix peak at 4096³ and 8192³"
+PEAK_FP32_MATRIX_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/api.cpp",
+                  "tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="square8192_uniform")
+    p.add_argument("--kernel", default="auto")
+    p.add_argument("--also", default="square4096_uniform",
+                   help="comma-separated extra workloads timed the same way ('' for none)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def kernel_call(name: str):
+    """(callable(A, B, C), description) for a --kernel choice."""
+    import tiled_gemm_tgemm_amd as tg
+
+    if name == "auto":
+        return (lambda A, B, C: tg.sgemm(A, B, out=C)), "tgemm_sgemm"
+    if name == "naive":
+        return (lambda A, B, C: tg.sgemm(A, B, out=C, kernel="naive")), "tgemm_sgemm_naive"
+    if name.startswith("lds"):
+        tile = int(name[3:].split("p")[0])
+        pad = 1 if name.endswith("p1") else 0
+        return ((lambda A, B, C: tg.sgemm(A, B, out=C, kernel="lds", tile=tile, pad=pad)),
+                f"tgemm_sgemm_lds(tile={tile},pad={pad})")
+    if name.startswith("mfma:"):
+        v = name.split(":", 1)[1]
+        names = tg.variant_names()
+        idx = names.index(v) if v in names else int(v)
+        return ((lambda A, B, C: tg.sgemm(A, B, out=C, kernel="mfma", variant=idx)),
+                f"tgemm_sgemm_mfma({names[idx]})")
+    raise SystemExit(f"unknown --kernel {name}")
+
+
+def time_workload(w, kernel: str, steps: int, warmup: int):
+    """Time `steps` calls on resident inputs; returns a dict of measurements."""
+    import numpy as np
+    import torch
+
+    import tiled_gemm_tgemm_amd as tg
+    from tiled_gemm_tgemm_amd import workloads as wl
+
+    A_h, B_h = wl.make_inputs(w)
+    A = torch.from_numpy(A_h).cuda()
+    B = torch.from_numpy(B_h).cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    call, desc = kernel_call(kernel)
+    variant = None
+    if kernel == "auto":
+        v = tg.tgemm_sgemm_variant_for(w.M, w.N, w.K, A.data_ptr(), w.K, B.data_ptr(), w.N,
+                                       C.data_ptr(), w.N)
+        variant = tg.tgemm_mfma_variant_name(v)
+    for _ in range(warmup):
+        call(A, B, C)
+    stream = torch.cuda.current_stream()  # the stream every call is queued on
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call(A, B, C)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+    wall_ms = (t1 - t0) * 1e3 / steps
+    kernel_ms = float(per.mean())
+    return {
+        "workload": w, "A_host": A_h, "B_host": B_h, "C": C, "desc": desc, "variant": variant,
+        "wall_ms": wall_ms, "kernel_ms": kernel_ms,
+        "kernel_ms_min": float(per.min()), "kernel_ms_median": float(np.median(per)),
+        "kernel_ms_p90": float(np.percentile(per, 90)),
+        "tflops_wall": w.flops / (wall_ms * 1e-3) / 1e12,
+        "tflops_kernel": w.flops / (kernel_ms * 1e-3) / 1e12,
+    }
+
+
+def traffic_for(workload_name: str, kernel_desc: str):
+    """Measured HBM bytes per launch from the committed counter summary, or None."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    with open(TRAFFIC_RECORD) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    entry = rec.get("workloads", {}).get(workload_name)
+    if not entry:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(m, target_s: float):
+    """The oracle on whole rows of the same product, sized to ~target_s."""
+    import numpy as np
+
+    import oracle
+
+    w = m["workload"]
+    A, B = m["A_host"], m["B_host"]
+    rows = 2
+    t = 0.0
+    while True:
+        t0 = time.perf_counter()
+        P, S = oracle.gemm_window(A, B, 0, rows, 0, w.N)
+        t = time.perf_counter() - t0
+        if t >= target_s or rows >= w.M:
+            break
+        # scale the sample to the target from the measured rate
+        want = int(rows * min(max(target_s / max(t, 1e-3), 2.0), 64.0))
+        rows = min(w.M, max(rows + 1, want))
+        if t * want / rows > 3 * target_s:
+            break
+    macs = rows * w.N * w.K
+    C_rows = m["C"][:rows].cpu().numpy().astype(np.float64)
+    ok = bool(np.all(np.abs(C_rows - P) <= 4.0 * w.K * 2.0 ** -24 * S))
+    return {
+        "value": 2.0 * macs / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} rows of C ({rows}x{w.N}, K={w.K}) of {w.name}: float64 sums "
+                  f"with exact float32 products, plus the sums of |products|; {t:.2f} s",
+        "sample_rows_within_bound": ok,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs "
+              "are outside this build.", file=sys.stderr)
+        return 2
+    import torch
+
+    from tiled_gemm_tgemm_amd import _lib, build, workloads as wl
+
+    if not os.path.exists(_lib.LIBRARY):
+        build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    props = torch.cuda.get_device_properties(0)
+
+    w = wl.WORKLOADS[args.workload]
+    m = time_workload(w, args.kernel, args.steps, args.warmup)
+    traffic = traffic_for(w.name, m["desc"]) if args.kernel == "auto" else None
+    achieved = m["tflops_kernel"]
+    line = {
+        "metric": METRIC,
+        "value": round(m["tflops_wall"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "values": w.dist,
+                   "seed": w.seed, "kernel": m["desc"], "variant": m["variant"]},
+        "pct_of_fp32_matrix_peak": round(100.0 * m["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MATRIX_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_ms": {"mean": round(m["kernel_ms"], 4), "min": round(m["kernel_ms_min"], 4),
+                      "median": round(m["kernel_ms_median"], 4), "p90": round(m["kernel_ms_p90"], 4)},
+        "algorithmic_hbm_gbs": round(w.algorithmic_bytes / (m["kernel_ms"] * 1e-3) / 1e9, 1),
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+    }
+    also = {}
+    for name in [x for x in args.also.split(",") if x and x != w.name]:
+        wa = wl.WORKLOADS[name]
+        ma = time_workload(wa, args.kernel, args.steps, args.warmup)
+        also[name] = {
+            "tflops": round(ma["tflops_wall"], 3),
+            "ms_per_step": round(ma["wall_ms"], 4),
+            "pct_of_fp32_matrix_peak": round(100.0 * ma["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2),
+            "kernel_ms_mean": round(ma["kernel_ms"], 4),
+            "roofline_frac": round(ma["tflops_kernel"] / PEAK_FP32_MATRIX_TFLOPS, 4),
+            "algorithmic_hbm_gbs": round(wa.algorithmic_bytes / (ma["kernel_ms"] * 1e-3) / 1e9, 1),
+            "variant": ma["variant"],
+        }
+        del ma
+    if also:
+        line["also"] = also
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(m, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

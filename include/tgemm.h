@@ -1,0 +1,141 @@
+/*
+ * libtgemm — single-precision C = A·B on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the dense product of page 1 ("[Multi-Core & GPU
+ * Programming] CUDA - Matrix Multiplication", section [Matrix
+ * Multiplication]): every output is the sum over k of one row of the left
+ * matrix times one column of the right one.  The pages call the matrices
+ * M, N, P and the size Width; here they are A (M×K), B (K×N) and C (M×N),
+ * and M, N, K are sizes.
+ *
+ * Conventions shared by every compute entry point below
+ * ------------------------------------------------------
+ * Layout      Row-major float32 with leading dimensions counted in elements:
+ *             A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j]
+ *             (page 1, section [Coalescing], indexes M as M[row*width + k]).
+ *             Requires lda >= max(1,K), ldb >= max(1,N), ldc >= max(1,N).
+ * Semantics   C(i,j) = sum_{k<K} A(i,k)·B(k,j).  C is overwritten, never read
+ *             (page 1 keeps the sum in a register and writes the output once,
+ *             at the end).  K = 0 sets C to +0.0; M = 0 or N = 0 is a no-op.
+ * Memory      A, B and C are device pointers (hipMalloc, or a torch CUDA
+ *             tensor's storage) owned by the caller.  The library allocates
+ *             nothing and keeps no per-call state.  C must not overlap A or B.
+ * Streams     Work is queued on `stream` (NULL = the default stream) and the
+ *             call returns without waiting; results are ready once the
+ *             stream has been synchronised (page 3, "CUDA.3 Writing CUDA SIMT
+ *             Kernels", Global Memory: kernels hand results back only through
+ *             device memory).
+ * Errors      Argument problems are reported before anything is queued, and C
+ *             is then left untouched.  TGEMM_ERROR_HIP means the launch itself
+ *             failed.  A fault inside a kernel shows up at the caller's next
+ *             stream synchronisation, as for any asynchronous HIP work.
+ *             Nothing is printed and no C++ exception crosses this interface.
+ * Sizes       M, N, K up to 2^31 - 1; element offsets are 64-bit.
+ * Threads     All entry points are re-entrant and may be called concurrently
+ *             on different streams.
+ * Rounding    The tiled MFMA kernels sum in an order of their own; for real
+ *             inputs the result lies within 4·K·2^-24·sum_k|A(i,k)·B(k,j)| of
+ *             the exact one, and integer-valued inputs whose partial sums stay
+ *             below 2^24 in magnitude give the exact result.  The two
+ *             one-product-per-step kernels (naive, LDS-tiled) add the products
+ *             one fused multiply-add at a time in ascending k.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as the HIP runtime's, so either header may come first. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum tgemm_status {
+    TGEMM_SUCCESS = 0,
+    TGEMM_ERROR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer or overlap */
+    TGEMM_ERROR_NOT_SUPPORTED = 2, /* a size above 2^31-1, or an unknown kernel choice */
+    TGEMM_ERROR_HIP = 3            /* the HIP runtime refused the launch */
+} tgemm_status_t;
+
+/*
+ * C = A·B with the tiled matrix-core kernel: the product of page 1 computed
+ * tile by tile as in page 1's section [Shared Memory] and page 2 ("Lec 29 ·
+ * GPU Architecture (2)") §1.2 — tiles of A and B staged through on-chip
+ * memory in phases, one barrier per phase, sums kept in registers — with
+ * the tile shape chosen from M, N, K and the operands' alignment.
+ * Arguments and errors: see the conventions above.
+ */
+tgemm_status_t tgemm_sgemm(int64_t M, int64_t N, int64_t K,
+                           const float *A, int64_t lda,
+                           const float *B, int64_t ldb,
+                           float *C, int64_t ldc, hipStream_t stream);
+
+/*
+ * Same product with an explicitly chosen matrix-core tile configuration,
+ * 0 <= variant < tgemm_mfma_variant_count().  Variants whose vector loads
+ * need 16-byte alignment return TGEMM_ERROR_NOT_SUPPORTED when A, B, C,
+ * lda, ldb, ldc, K or N do not allow them (see tgemm_mfma_variant_name).
+ */
+tgemm_status_t tgemm_sgemm_mfma(int64_t M, int64_t N, int64_t K,
+                                const float *A, int64_t lda,
+                                const float *B, int64_t ldb,
+                                float *C, int64_t ldc, int variant, hipStream_t stream);
+
+/* Number of matrix-core tile configurations. */
+int tgemm_mfma_variant_count(void);
+
+/*
+ * Static description of a variant, e.g. "m256n256k32_w2x2_vec4"
+ * (macro tile 256×256, depth 32 per phase, 2×2 wavefronts, 16-byte loads);
+ * NULL for an index out of range.
+ */
+const char *tgemm_mfma_variant_name(int variant);
+
+/* The variant tgemm_sgemm would run for these arguments; -1 if none applies. */
+int tgemm_sgemm_variant_for(int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            const float *C, int64_t ldc);
+
+/*
+ * Ablation 1 — one thread per output (page 1, section [Matrix
+ * Multiplication], the simplest kernel and "Work Flow"; page 2 §1.2, naive
+ * kernel): a 16×16 thread block per 16×16 output tile; each thread reads its
+ * row of A and column of B straight from device memory and adds one fused
+ * multiply-add per k in ascending order.  Arguments and errors as above.
+ */
+tgemm_status_t tgemm_sgemm_naive(int64_t M, int64_t N, int64_t K,
+                                 const float *A, int64_t lda,
+                                 const float *B, int64_t ldb,
+                                 float *C, int64_t ldc, hipStream_t stream);
+
+/*
+ * Ablation 2 — the shared-memory tiled kernel (page 1, section [Shared
+ * Memory], "Work Flow - Compute Block(0, 0)" and "Tiled Matrix
+ * Multiplication Kernel"; page 2 §1.2): tile×tile threads per block, two
+ * tile×tile on-chip tiles; per phase every thread copies one element of A
+ * and one of B, the block synchronises, every thread adds the tile's
+ * products to its register sum (one fused multiply-add per k, ascending),
+ * and the block synchronises again.  Out-of-range elements load as zero.
+ * tile is 2, 8, 16 or 32.  pad = 1 adds one word to each tile row
+ * (page 2 §1.4, tile[32][33]); pad = 0 does not.  Other values:
+ * TGEMM_ERROR_NOT_SUPPORTED.  Arguments and errors otherwise as above.
+ */
+tgemm_status_t tgemm_sgemm_lds(int64_t M, int64_t N, int64_t K,
+                               const float *A, int64_t lda,
+                               const float *B, int64_t ldb,
+                               float *C, int64_t ldc, int tile, int pad, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *tgemm_status_string(tgemm_status_t status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int tgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

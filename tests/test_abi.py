@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports exactly what
+include/tgemm.h declares, the header stands alone in C and C++, and every
+argument check returns its documented status before any HIP call is made.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_gemm_tgemm_amd as tg
+from tiled_gemm_tgemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIBRARY):
+        from tiled_gemm_tgemm_amd import build
+
+        build.build()
+    return tg.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(tgemm_\w+)\s*\(", text))
+
+
+def test_header_declares_the_binding(lib):
+    names = declared_functions()
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(tgemm_\w+)$", out, flags=re.M))
+    assert declared_functions() <= exported
+    for name in declared_functions():
+        assert hasattr(lib, name)
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c11"), ("g++", "-std=c++17")])
+def test_header_compiles_alone(tmp_path, compiler, std):
+    ext = "c" if compiler == "gcc" else "cpp"
+    src = tmp_path / f"use.{ext}"
+    src.write_text('#include "tgemm.h"\nint main(void) { return tgemm_version() > 0 ? 0 : 1; }\n')
+    subprocess.run([compiler, std, "-Wall", "-Werror", "-pedantic", f"-I{ROOT}/include", "-c",
+                    str(src), "-o", str(tmp_path / "use.o")], check=True)
+
+
+def test_static_queries(lib):
+    assert tg.tgemm_version() == 100
+    n = tg.tgemm_mfma_variant_count()
+    assert n >= 6
+    names = tg.variant_names()
+    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_w\dx\d_vec[14]", x) for x in names)
+    assert tg.tgemm_mfma_variant_name(n) is None and tg.tgemm_mfma_variant_name(-1) is None
+    for st in range(4):
+        assert tg.tgemm_status_string(st)
+    assert "unknown" in tg.tgemm_status_string(99)
+
+
+# Fake device addresses: argument checks never dereference them, and every
+# case below is rejected (or finishes as a no-op) before any HIP call.
+A_, B_, C_ = 0x10000000, 0x20000000, 0x30000000
+INVALID, UNSUPPORTED = tg.TGEMM_ERROR_INVALID_VALUE, tg.TGEMM_ERROR_NOT_SUPPORTED
+
+ENTRY = {
+    "sgemm": lambda *a: tg.tgemm_sgemm(*a, None),
+    "naive": lambda *a: tg.tgemm_sgemm_naive(*a, None),
+    "lds": lambda *a: tg.tgemm_sgemm_lds(*a, 16, 1, None),
+    "mfma": lambda *a: tg.tgemm_sgemm_mfma(*a, 0, None),
+}
+
+CASES = [
+    # (M, N, K, A, lda, B, ldb, C, ldc) -> status
+    ((-1, 4, 4, A_, 4, B_, 4, C_, 4), INVALID),
+    ((4, -1, 4, A_, 4, B_, 4, C_, 4), INVALID),
+    ((4, 4, -1, A_, 4, B_, 4, C_, 4), INVALID),
+    ((4, 4, 8, A_, 7, B_, 4, C_, 4), INVALID),      # lda < K
+    ((4, 8, 4, A_, 4, B_, 7, C_, 8), INVALID),      # ldb < N
+    ((4, 8, 4, A_, 4, B_, 8, C_, 7), INVALID),      # ldc < N
+    ((4, 4, 4, A_, 0, B_, 4, C_, 4), INVALID),      # ld below 1
+    ((4, 4, 4, 0, 4, B_, 4, C_, 4), INVALID),       # null A
+    ((4, 4, 4, A_, 4, 0, 4, C_, 4), INVALID),       # null B
+    ((4, 4, 4, A_, 4, B_, 4, 0, 4), INVALID),       # null C
+    ((4, 4, 4, A_ + 2, 4, B_, 4, C_, 4), INVALID),  # misaligned A
+    ((4, 4, 4, A_, 4, B_, 4, A_ + 8, 4), INVALID),  # C overlaps A
+    ((4, 4, 4, A_, 4, B_, 4, B_ + 60, 4), INVALID),  # C overlaps B's last element
+    ((2 ** 31, 4, 4, A_, 4, B_, 4, C_, 4), UNSUPPORTED),
+    ((4, 4, 2 ** 31, A_, 2 ** 31, B_, 4, C_, 4), UNSUPPORTED),
+    ((0, 4, 4, A_, 4, B_, 4, C_, 4), tg.TGEMM_SUCCESS),  # M = 0: nothing to do
+    ((4, 0, 4, A_, 4, B_, 1, C_, 1), tg.TGEMM_SUCCESS),  # N = 0
+    ((0, 4, 4, 0, 4, 0, 4, 0, 4), tg.TGEMM_SUCCESS),     # no-op ignores pointers
+]
+
+
+@pytest.mark.parametrize("entry", sorted(ENTRY))
+@pytest.mark.parametrize("args,status", CASES)
+def test_argument_checks(lib, entry, args, status):
+    assert ENTRY[entry](*args) == status
+
+
+def test_kernel_choice_checks(lib):
+    args = (64, 64, 64, A_, 64, B_, 64, C_, 64)
+    n = tg.tgemm_mfma_variant_count()
+    assert tg.tgemm_sgemm_mfma(*args, n, None) == UNSUPPORTED
+    assert tg.tgemm_sgemm_mfma(*args, -1, None) == UNSUPPORTED
+    for tile, pad in [(3, 0), (64, 0), (16, 2), (0, 0)]:
+        assert tg.tgemm_sgemm_lds(*args, tile, pad, None) == UNSUPPORTED
+    # a 16-byte-load variant on operands that cannot take them
+    vec4 = [i for i, name in enumerate(tg.variant_names()) if name.endswith("vec4")]
+    assert tg.tgemm_sgemm_mfma(64, 63, 64, A_, 64, B_, 63, C_, 63, vec4[0], None) == UNSUPPORTED
+    assert tg.tgemm_sgemm_mfma(64, 64, 63, A_, 63, B_, 64, C_, 64, vec4[0], None) == UNSUPPORTED
+    assert tg.tgemm_sgemm_mfma(64, 64, 64, A_ + 4, 64, B_, 64, C_, 64, vec4[0], None) == UNSUPPORTED
+
+
+def test_variant_choice(lib):
+    names = tg.variant_names()
+
+    def chosen(M, N, K, a=A_, lda=None, ldb=None, ldc=None):
+        v = tg.tgemm_sgemm_variant_for(M, N, K, a, lda or K, B_, ldb or N, C_, ldc or N)
+        return names[v] if v >= 0 else None
+
+    assert chosen(8192, 8192, 8192) == "m256n256k32_w2x2_vec4"
+    assert chosen(4096, 4096, 4096) == "m256n256k32_w2x2_vec4"
+    assert chosen(512, 512, 512).endswith("vec4")
+    assert chosen(1024, 1024, 1024).endswith("vec4")
+    assert chosen(3000, 5000, 1000).endswith("vec4")
+    assert chosen(7, 5, 3).endswith("vec1")          # K, N not multiples of 4
+    assert chosen(64, 64, 64, a=A_ + 4).endswith("vec1")  # A not 16-byte aligned
+    assert chosen(0, 4, 4) is None and chosen(4, 4, 0) is None
+    assert tg.tgemm_sgemm_variant_for(4, 4, 4, A_, 2, B_, 4, C_, 4) == -1

@@ -1,0 +1,383 @@
+"""GPU parity: every kernel through the C ABI against the CPU oracle.
+
+Acceptance (the product's definition gives no tolerance, so it is derived
+from the arithmetic):
+* integer-valued inputs whose partial sums stay below 2^24: every float32
+  partial sum is exact in any order, so the result must equal the exact
+  integer product element for element;
+* real inputs: |C_ij − P_ij| <= 4·K·2^-24·S_ij with S_ij = sum_k |A_ik·B_kj|,
+  compared in float64 (4× the classical bound for recursive float32
+  summation, leaving room for any order and the matrix cores' internal
+  rounding);
+* the two one-product-per-step ablation kernels must also equal, bit for
+  bit, the oracle's float32 sequential fused-multiply-add model.
+
+Workloads are the seeded synthetic ones of tiled_gemm_tgemm_amd.workloads;
+the two largest are checked on sampled 64×64 blocks plus full row and column
+checksums (4096² also in full), in the launch configuration the benchmark
+times (tgemm_sgemm on contiguous operands).
+"""
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import tiled_gemm_tgemm_amd as tg
+from tiled_gemm_tgemm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TWO_M24 = 2.0 ** -24
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+    tg.library()  # raises if libtgemm.so is missing
+    yield
+
+
+VARIANTS = None
+
+
+def variants():
+    global VARIANTS
+    if VARIANTS is None:
+        VARIANTS = tg.variant_names()
+    return VARIANTS
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run(A, B, kernel="auto", **kw):
+    C = tg.sgemm(dev(A), dev(B), kernel=kernel, **kw)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def assert_within_bound(C, P, S, K, what=""):
+    C = C.astype(np.float64)
+    assert np.all(np.isfinite(C)), f"{what}: non-finite output"
+    err = np.abs(C - P)
+    bound = 4.0 * K * TWO_M24 * S
+    bad = err > bound
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        pytest.fail(f"{what}: {bad.sum()} elements outside the bound; first ({i},{j}): "
+                    f"C={C[i, j]!r} P={P[i, j]!r} bound={bound[i, j]!r}")
+    ratio = float(np.max(err / np.maximum(K * TWO_M24 * S, 1e-300))) if err.size else 0.0
+    return ratio
+
+
+def assert_exact(C, P_int, what=""):
+    got = C.astype(np.float64)
+    want = P_int.astype(np.float64)
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        i, j = bad[0]
+        pytest.fail(f"{what}: {len(bad)} elements differ; first ({i},{j}) {got[i, j]} vs {want[i, j]}")
+
+
+def int_inputs(M, N, K, seed):
+    A, B, _ = wl.random_matrices(M, N, K, "int4", seed)
+    return A, B
+
+
+def vec4_shape(M, N, K):
+    return K % 4 == 0 and N % 4 == 0
+
+
+def auto_variant(M, N, K):
+    """Name of the variant tgemm_sgemm picks for contiguous, aligned operands."""
+    v = tg.tgemm_sgemm_variant_for(M, N, K, 1 << 20, K, 1 << 36, N, 1 << 44, N)
+    return variants()[v] if v >= 0 else None
+
+
+# ------------------------------------------------------------ the workloads
+
+def test_square512_uniform_all_kernels():
+    w = wl.WORKLOADS["square512_uniform"]
+    A, B = wl.make_inputs(w)
+    P, S = oracle.gemm(A, B)
+    fma = oracle.gemm_fma_f32(A, B)
+    log(f"{w.name}: auto")
+    assert_within_bound(run(A, B), P, S, w.K, "auto")
+    for v, name in enumerate(variants()):
+        log(f"{w.name}: {name}")
+        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, name)
+    log(f"{w.name}: naive")
+    C = run(A, B, "naive")
+    assert np.array_equal(C, fma), "naive differs from the sequential fma model"
+    for tile, pad in itertools.product((8, 16, 32), (0, 1)):
+        log(f"{w.name}: lds tile={tile} pad={pad}")
+        C = run(A, B, "lds", tile=tile, pad=pad)
+        assert np.array_equal(C, fma), f"lds{tile} pad{pad} differs from the fma model"
+
+
+def test_square1024_int4_bit_exact():
+    w = wl.WORKLOADS["square1024_int4"]
+    A, B = wl.make_inputs(w)
+    Pi = oracle.gemm_i64(A, B)
+    P, _ = oracle.gemm(A, B, with_abs=False)
+    assert np.array_equal(P, Pi.astype(np.float64))  # the two oracle paths agree
+    log(f"{w.name}: auto")
+    assert_exact(run(A, B), Pi, "auto")
+    for v, name in enumerate(variants()):
+        log(f"{w.name}: {name}")
+        assert_exact(run(A, B, "mfma", variant=v), Pi, name)
+    log(f"{w.name}: naive / lds")
+    assert_exact(run(A, B, "naive"), Pi, "naive")
+    assert_exact(run(A, B, "lds", tile=16, pad=1), Pi, "lds16")
+    assert_exact(run(A, B, "lds", tile=32, pad=0), Pi, "lds32")
+
+
+def test_rect3000x1000x5000_normal_masked_edges():
+    w = wl.WORKLOADS["rect3000x1000x5000_normal"]
+    A, B = wl.make_inputs(w)
+    log(f"{w.name}: oracle")
+    P, S = oracle.gemm(A, B)
+    log(f"{w.name}: auto")
+    assert_within_bound(run(A, B), P, S, w.K, "auto")
+    for v, name in enumerate(variants()):
+        log(f"{w.name}: {name}")
+        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, name)
+
+
+def check_sampled(C, A, B, blocks, K, what):
+    for (r, c), (P, S) in zip(blocks, oracle.gemm_blocks(A, B, blocks, 64)):
+        assert_within_bound(C[r:r + 64, c:c + 64], P, S, K, f"{what} block ({r},{c})")
+    row, rowabs, col, colabs = oracle.checksums(A, B)
+    C64 = C.astype(np.float64)
+    M, N = C.shape
+    rs, cs = C64.sum(axis=1), C64.sum(axis=0)
+    # each sum of C inherits the per-element bound; float64 rounding of the
+    # sums themselves adds at most (N+K)·2^-53 of the magnitudes involved
+    slack_r = 4 * K * TWO_M24 * rowabs + 2 * (N + K) * 2.0 ** -53 * (rowabs + np.abs(C64).sum(1))
+    slack_c = 4 * K * TWO_M24 * colabs + 2 * (M + K) * 2.0 ** -53 * (colabs + np.abs(C64).sum(0))
+    assert np.all(np.abs(rs - row) <= slack_r), f"{what}: row checksums"
+    assert np.all(np.abs(cs - col) <= slack_c), f"{what}: column checksums"
+
+
+def test_square4096_uniform_full():
+    w = wl.WORKLOADS["square4096_uniform"]
+    A, B, blocks = wl.make_inputs_and_blocks(w)
+    log(f"{w.name}: auto ({auto_variant(w.M, w.N, w.K)})")
+    C = run(A, B)
+    check_sampled(C, A, B, blocks, w.K, w.name)
+    log(f"{w.name}: full oracle")
+    P, S = oracle.gemm(A, B)
+    assert_within_bound(C, P, S, w.K, w.name)
+
+
+def test_square8192_uniform_sampled():
+    w = wl.WORKLOADS["square8192_uniform"]
+    A, B, blocks = wl.make_inputs_and_blocks(w)
+    log(f"{w.name}: auto ({auto_variant(w.M, w.N, w.K)})")
+    C = run(A, B)
+    check_sampled(C, A, B, blocks, w.K, w.name)
+
+
+# ------------------------------------------------------------ edges, in integers
+
+EDGE = [1, 2, 3, 7, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def edge_triples(count, seed, mult4=False):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M, N, K = (int(x) for x in rng.choice(EDGE, 3))
+        if mult4:
+            N, K = (N + 3) // 4 * 4, (K + 3) // 4 * 4
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", edge_triples(24, 11) + [(1, 1, 1), (257, 257, 257), (300, 7, 513)])
+def test_edge_shapes_integer_exact(M, N, K):
+    A, B = int_inputs(M, N, K, M * 1000003 + N * 1009 + K)
+    Pi = oracle.gemm_i64(A, B)
+    log(f"edge {M}x{N}x{K}")
+    assert_exact(run(A, B), Pi, "auto")
+    for v, name in enumerate(variants()):
+        if name.endswith("vec4") and not vec4_shape(M, N, K):
+            continue
+        assert_exact(run(A, B, "mfma", variant=v), Pi, name)
+    assert_exact(run(A, B, "naive"), Pi, "naive")
+    for tile in (2, 16, 32) if max(M, N) <= 64 else (16, 32):
+        assert_exact(run(A, B, "lds", tile=tile, pad=1), Pi, f"lds{tile}")
+
+
+@pytest.mark.parametrize("M,N,K", edge_triples(16, 12, mult4=True) + [(256, 256, 36), (255, 260, 4)])
+def test_edge_shapes_vector_loads_exact(M, N, K):
+    A, B = int_inputs(M, N, K, M * 7 + N * 11 + K * 13)
+    Pi = oracle.gemm_i64(A, B)
+    log(f"edge vec4 {M}x{N}x{K}")
+    for v, name in enumerate(variants()):
+        assert_exact(run(A, B, "mfma", variant=v), Pi, name)
+
+
+def guarded(x, rows_extra, cols_extra, fill):
+    """x embedded top-left in a larger buffer filled with `fill`; returns (big, view)."""
+    r, c = x.shape
+    big = torch.full((r + rows_extra, c + cols_extra), fill, dtype=torch.float32, device="cuda")
+    big[:r, :c] = dev(x)
+    return big, big[:r, :c]
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(65, 33, 31, 5), (130, 68, 36, 4), (257, 129, 40, 8),
+                                       (1, 1, 1, 3), (64, 256, 100, 4)])
+def test_guard_bands(M, N, K, pad):
+    """NaN around A and B (wider leading dimensions, extra rows) and sentinels
+    around C: a NaN in C means something outside A or B was used, a changed
+    sentinel means a write outside C."""
+    A, B = int_inputs(M, N, K, 5 + M + N + K)
+    Pi = oracle.gemm_i64(A, B)
+    kernels = [("auto", {})] + [("mfma", {"variant": v}) for v, n in enumerate(variants())
+                                if not (n.endswith("vec4") and (pad % 4 or not vec4_shape(M, N, K)))]
+    kernels += [("naive", {}), ("lds", {"tile": 16, "pad": 1})]
+    for kernel, kw in kernels:
+        log(f"guard {M}x{N}x{K} pad {pad}: {kernel} {kw}")
+        _, Av = guarded(A, 3, pad, float("nan"))
+        _, Bv = guarded(B, 3, pad, float("nan"))
+        Cbig, Cv = guarded(np.zeros((M, N), np.float32), 2, pad, 12345.0)
+        tg.sgemm(Av, Bv, out=Cv, kernel=kernel, **kw)
+        torch.cuda.synchronize()
+        big = Cbig.cpu().numpy()
+        assert_exact(big[:M, :N], Pi, f"{kernel} {kw}")
+        outside = np.ones(big.shape, bool)
+        outside[:M, :N] = False
+        assert np.all(big[outside] == 12345.0), f"{kernel} {kw} wrote outside C"
+
+
+# ------------------------------------------------------------ identities and invariants
+
+def test_identities_bit_exact_real_inputs():
+    """I·B = B, A·I = A and permutations are exact for any finite input: each
+    output is one product by 1 plus exact zeros, in any summation order."""
+    rng = np.random.default_rng(21)
+    for (M, N, K) in [(200, 136, 72), (64, 64, 64), (33, 65, 129)]:
+        A, B, _ = wl.random_matrices(M, N, K, "normal", 31)
+        for kernel, kw in [("auto", {})] + [("mfma", {"variant": v}) for v, n in enumerate(variants())
+                                             if not (n.endswith("vec4") and not vec4_shape(M, N, K))]:
+            log(f"identities {M}x{N}x{K} {kernel} {kw}")
+            assert np.array_equal(run(np.eye(M, dtype=np.float32), A, kernel, **kw), A)
+            assert np.array_equal(run(B, np.eye(N, dtype=np.float32), kernel, **kw), B)
+            perm = rng.permutation(K)
+            Pm = np.eye(K, dtype=np.float32)[perm]
+            assert np.array_equal(run(Pm, B, kernel, **kw), B[perm])
+            assert np.array_equal(run(A, np.ascontiguousarray(Pm.T), kernel, **kw), A[:, perm])
+
+
+def test_one_hot_locates_every_position():
+    M, N, K = 130, 100, 70
+    rng = np.random.default_rng(3)
+    for _ in range(6):
+        i0, k0, j0 = int(rng.integers(M)), int(rng.integers(K)), int(rng.integers(N))
+        A = np.zeros((M, K), np.float32)
+        B = np.zeros((K, N), np.float32)
+        A[i0, k0] = 3.0
+        B[k0, j0] = -5.0
+        want = np.zeros((M, N), np.float32)
+        want[i0, j0] = -15.0
+        for v, name in enumerate(variants()):
+            if name.endswith("vec4") and not vec4_shape(M, N, K):
+                continue
+            assert np.array_equal(run(A, B, "mfma", variant=v), want), (name, i0, k0, j0)
+
+
+def test_transpose_symmetry():
+    """(A·B)ᵀ == Bᵀ·Aᵀ: exact on integers, within twice the bound on reals."""
+    A, B = int_inputs(96, 160, 200, 77)
+    C = run(A, B)
+    Ct = run(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T))
+    assert np.array_equal(C.T, Ct)
+    A, B, _ = wl.random_matrices(96, 160, 200, "uniform", 78)
+    _, S = oracle.gemm(A, B)
+    C = run(A, B).astype(np.float64)
+    Ct = run(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T)).astype(np.float64)
+    assert np.all(np.abs(C.T - Ct) <= 8 * 200 * TWO_M24 * S.T)
+
+
+def test_invariants_scaling_sign_determinism():
+    A, B, _ = wl.random_matrices(320, 288, 264, "uniform", 91)
+    for kernel, kw in [("auto", {}), ("naive", {}), ("lds", {"tile": 16, "pad": 1})] + \
+            [("mfma", {"variant": v}) for v in range(len(variants()))]:
+        log(f"invariants {kernel} {kw}")
+        C = run(A, B, kernel, **kw)
+        assert np.array_equal(C, run(A, B, kernel, **kw)), "not deterministic"
+        assert np.array_equal(run(A * np.float32(8), B * np.float32(0.25), kernel, **kw), C * 2)
+        assert np.array_equal(run(-A, B, kernel, **kw), -C)
+
+
+def test_worked_example_tile2():
+    """Page 1's 4x4 example through the TILE_WIDTH = 2 tiled kernel: values
+    M_ik = 4i+k+1, N_kj = 4k+j+1; closed form (4i+1)(4j+28) + 6j + 62."""
+    Mx = np.array([[4 * i + k + 1 for k in range(4)] for i in range(4)], np.float32)
+    Nx = np.array([[4 * k + j + 1 for j in range(4)] for k in range(4)], np.float32)
+    want = np.array([[(4 * i + 1) * (4 * j + 28) + 6 * j + 62 for j in range(4)] for i in range(4)],
+                    np.float32)
+    for pad in (0, 1):
+        assert np.array_equal(run(Mx, Nx, "lds", tile=2, pad=pad), want)
+    assert np.array_equal(run(Mx, Nx, "naive"), want)
+    for v, name in enumerate(variants()):
+        assert np.array_equal(run(Mx, Nx, "mfma", variant=v), want), name
+
+
+# ------------------------------------------------------------ ABI on the device
+
+def test_zero_k_fills_positive_zero_and_empty_is_noop():
+    for kernel, kw in [("auto", {}), ("naive", {}), ("lds", {"tile": 16, "pad": 0}),
+                       ("mfma", {"variant": 0})]:
+        C = torch.full((5, 12), float("nan"), device="cuda")
+        tg.sgemm(torch.empty((5, 0), device="cuda"), torch.empty((0, 12), device="cuda"), out=C,
+                 kernel=kernel, **kw)
+        torch.cuda.synchronize()
+        c = C.cpu().numpy()
+        assert np.all(c == 0) and not np.any(np.signbit(c)), kernel
+        C = torch.full((0, 12), 7.0, device="cuda")
+        tg.sgemm(torch.ones((0, 3), device="cuda"), torch.ones((3, 12), device="cuda"), out=C,
+                 kernel=kernel, **kw)
+    sentinel = torch.full((4, 4), 7.0, device="cuda")
+    st = tg.tgemm_sgemm(4, 4, 4, sentinel.data_ptr(), 4, sentinel.data_ptr(), 4, 0, 4, None)
+    assert st == tg.TGEMM_ERROR_INVALID_VALUE
+
+
+def test_errors_leave_c_untouched():
+    A = dev(np.ones((8, 8), np.float32))
+    C = torch.full((8, 8), 3.0, device="cuda")
+    st = tg.tgemm_sgemm(8, 8, 8, A.data_ptr(), 7, A.data_ptr(), 8, C.data_ptr(), 8, None)
+    assert st == tg.TGEMM_ERROR_INVALID_VALUE
+    st = tg.tgemm_sgemm(8, 8, 8, A.data_ptr(), 8, A.data_ptr(), 8, A.data_ptr(), 8, None)
+    assert st == tg.TGEMM_ERROR_INVALID_VALUE  # C overlaps A
+    torch.cuda.synchronize()
+    assert torch.all(C == 3.0)
+
+
+def test_non_default_stream():
+    A, B = int_inputs(300, 260, 180, 5)
+    Pi = oracle.gemm_i64(A, B)
+    s = torch.cuda.Stream()
+    dA, dB = dev(A), dev(B)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        C = tg.sgemm(dA, dB)
+    s.synchronize()
+    assert_exact(C.cpu().numpy(), Pi, "side stream")
+    C2 = torch.empty_like(C)
+    tg.sgemm(dA, dB, out=C2, stream=s.cuda_stream)
+    s.synchronize()
+    assert torch.equal(C, C2)

@@ -1,5 +1,95 @@
 """tiled_gemm_tgemm_amd: fp32 C = A·B for one MI355X (gfx950), hand-written HIP.
 
 The compute lives in the C-ABI library libtgemm.so (sources in csrc/,
-declarations in include/tgemm.h); this package only marshals arguments.
+declarations in include/tgemm.h).  ``_lib`` exposes the C entry points under
+their own names; ``sgemm`` below is the same call for torch tensors, with
+torch used for device memory and the current stream only.
+
+Nothing here loads the library at import time; the first call does, and it
+raises if libtgemm.so has not been built (``python -m
+tiled_gemm_tgemm_amd.build``).
 """
+
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    TGEMM_ERROR_HIP,
+    TGEMM_ERROR_INVALID_VALUE,
+    TGEMM_ERROR_NOT_SUPPORTED,
+    TGEMM_SUCCESS,
+    TgemmError,
+    library,
+    tgemm_mfma_variant_count,
+    tgemm_mfma_variant_name,
+    tgemm_sgemm,
+    tgemm_sgemm_lds,
+    tgemm_sgemm_mfma,
+    tgemm_sgemm_naive,
+    tgemm_sgemm_variant_for,
+    tgemm_status_string,
+    tgemm_version,
+)
+
+KERNELS = ("auto", "mfma", "naive", "lds")
+
+
+def _operand(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 torch tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must live on a GPU")
+    if t.stride(1) != 1 and t.size(1) > 1:
+        raise ValueError(f"{name} must be row-major (unit stride along columns)")
+    return t
+
+
+def _ld(t):
+    return max(t.stride(0), t.size(1), 1)
+
+
+def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream=None):
+    """C = A·B for float32 CUDA tensors (row-major, any leading dimension).
+
+    kernel: "auto" (tgemm_sgemm), "mfma" (tgemm_sgemm_mfma with `variant`;
+    without one it is "auto"),
+    "naive" (tgemm_sgemm_naive) or "lds" (tgemm_sgemm_lds with tile/pad).
+    The call is queued on `stream` (default: torch's current stream) and
+    returns `out` without waiting.
+    """
+    import torch
+
+    A = _operand(A, "A")
+    B = _operand(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        out = _operand(out, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be {M}x{N}")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    args = (M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), out.data_ptr(), _ld(out))
+    if kernel == "auto" or (kernel == "mfma" and variant is None):
+        st = tgemm_sgemm(*args, stream)
+    elif kernel == "mfma":
+        st = tgemm_sgemm_mfma(*args, variant, stream)
+    elif kernel == "naive":
+        st = tgemm_sgemm_naive(*args, stream)
+    elif kernel == "lds":
+        st = tgemm_sgemm_lds(*args, tile, pad, stream)
+    else:
+        raise ValueError(f"kernel must be one of {KERNELS}")
+    if st != TGEMM_SUCCESS:
+        raise TgemmError(st, f"tgemm ({kernel})")
+    return out
+
+
+def variant_names():
+    """Names of the matrix-core tile configurations, by index."""
+    return [tgemm_mfma_variant_name(i) for i in range(tgemm_mfma_variant_count())]

@@ -1,0 +1,207 @@
+// C entry points of libtgemm: argument checks, quick returns, choice of the
+// matrix-core tile configuration, and one launch on the caller's stream.
+// The declarations, with the meaning of every argument, are in tgemm.h.
+#include "tgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "tgemm_kernels.h"
+
+namespace {
+
+using tgemm::GemmArgs;
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+int64_t max1(int64_t v) { return v > 1 ? v : 1; }
+
+// Byte range [lo, hi) spanned by a rows×cols row-major operand with leading
+// dimension ld (rows, cols >= 1).
+void span(const void *p, int64_t rows, int64_t cols, int64_t ld, uintptr_t &lo, uintptr_t &hi)
+{
+    lo = reinterpret_cast<uintptr_t>(p);
+    hi = lo + (uintptr_t)(((rows - 1) * ld + cols) * (int64_t)sizeof(float));
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+enum class Quick { kNone, kDone, kZeroFill };
+
+// Shared checks of every compute entry point.  On success `quick` says
+// whether the call is already complete (M or N zero) or only needs C zeroed
+// (K zero).
+tgemm_status_t validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                        const float *B, int64_t ldb, const float *C, int64_t ldc, Quick &quick)
+{
+    quick = Quick::kNone;
+    if (M < 0 || N < 0 || K < 0) return TGEMM_ERROR_INVALID_VALUE;
+    if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return TGEMM_ERROR_INVALID_VALUE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TGEMM_ERROR_NOT_SUPPORTED;
+    if (lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40 || ldc > (int64_t)1 << 40)
+        return TGEMM_ERROR_NOT_SUPPORTED;
+    if (M == 0 || N == 0) {
+        quick = Quick::kDone;
+        return TGEMM_SUCCESS;
+    }
+    if (C == nullptr || reinterpret_cast<uintptr_t>(C) % alignof(float)) return TGEMM_ERROR_INVALID_VALUE;
+    if (K == 0) {
+        quick = Quick::kZeroFill;
+        return TGEMM_SUCCESS;
+    }
+    if (A == nullptr || B == nullptr) return TGEMM_ERROR_INVALID_VALUE;
+    if (reinterpret_cast<uintptr_t>(A) % alignof(float) || reinterpret_cast<uintptr_t>(B) % alignof(float))
+        return TGEMM_ERROR_INVALID_VALUE;
+    uintptr_t a0, a1, b0, b1, c0, c1;
+    span(A, M, K, lda, a0, a1);
+    span(B, K, N, ldb, b0, b1);
+    span(C, M, N, ldc, c0, c1);
+    if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return TGEMM_ERROR_INVALID_VALUE;
+    return TGEMM_SUCCESS;
+}
+
+GemmArgs pack(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+              int64_t ldb, float *C, int64_t ldc)
+{
+    return GemmArgs{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc};
+}
+
+tgemm_status_t from_hip(hipError_t e) { return e == hipSuccess ? TGEMM_SUCCESS : TGEMM_ERROR_HIP; }
+
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// 16-byte loads need every row start 16-byte aligned and whole float4s
+// inside the logical row (K and N multiples of 4).
+bool vec4_ok(int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+             const float *C, int64_t ldc)
+{
+    return aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
+           ldc % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+}
+
+// Estimated cost of a configuration in units of one phase of one 64×64
+// wavefront sub-tile of matrix-core work on one SIMD.  Work-groups are dealt
+// to the 256 compute units in rounds; in a round each CU holds `resident`
+// work-groups (at most what its LDS allows) whose 4 wavefronts share its 4
+// SIMDs.  Edge tiles cost as much as full ones, which is what makes smaller
+// tiles win on small or ragged shapes.
+double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t cus = 256;
+    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    int64_t resident = (tiles + cus - 1) / cus;
+    if (resident > v.wg_per_cu) resident = v.wg_per_cu;
+    const int64_t rounds = (tiles + cus * resident - 1) / (cus * resident);
+    const int64_t phases = (K + v.bk - 1) / v.bk;
+    const double per_round = (double)phases * ((double)v.bm * v.bn / (64.0 * 64.0)) / 4.0 * resident;
+    // fixed cost per phase (barrier, LDS latency) and per work-group
+    const double overhead = (double)phases * 0.5 + 2.0;
+    return (double)rounds * (per_round + overhead);
+}
+
+int choose_variant(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                   int64_t ldb, const float *C, int64_t ldc)
+{
+    const int vec = vec4_ok(N, K, A, lda, B, ldb, C, ldc) ? 4 : 1;
+    int best = -1;
+    double best_cost = 0;
+    for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
+        const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
+        if (v->vec != vec) continue;
+        const double c = cost(*v, M, N, K);
+        if (best < 0 || c < best_cost) {
+            best = i;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+tgemm_status_t tgemm_sgemm_mfma(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                                const float *B, int64_t ldb, float *C, int64_t ldc, int variant,
+                                hipStream_t stream)
+{
+    const tgemm::MfmaVariant *v = tgemm::mfma_variant(variant);
+    if (v == nullptr) return TGEMM_ERROR_NOT_SUPPORTED;
+    Quick quick;
+    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if (v->vec == 4 && !vec4_ok(N, K, A, lda, B, ldb, C, ldc)) return TGEMM_ERROR_NOT_SUPPORTED;
+    return from_hip(v->launch(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
+}
+
+tgemm_status_t tgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                           const float *B, int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
+{
+    Quick quick;
+    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    const int variant = choose_variant(M, N, K, A, lda, B, ldb, C, ldc);
+    if (variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
+    return from_hip(tgemm::mfma_variant(variant)->launch(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
+}
+
+int tgemm_mfma_variant_count(void) { return tgemm::mfma_variant_count(); }
+
+const char *tgemm_mfma_variant_name(int variant)
+{
+    const tgemm::MfmaVariant *v = tgemm::mfma_variant(variant);
+    return v ? v->name : nullptr;
+}
+
+int tgemm_sgemm_variant_for(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                            const float *B, int64_t ldb, const float *C, int64_t ldc)
+{
+    Quick quick;
+    if (validate(M, N, K, A, lda, B, ldb, C, ldc, quick) != TGEMM_SUCCESS || quick != Quick::kNone)
+        return -1;
+    return choose_variant(M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+tgemm_status_t tgemm_sgemm_naive(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                                 const float *B, int64_t ldb, float *C, int64_t ldc,
+                                 hipStream_t stream)
+{
+    Quick quick;
+    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if ((M + 15) / 16 > 65535) return TGEMM_ERROR_NOT_SUPPORTED;  // grid rows limit
+    return from_hip(tgemm::launch_naive(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
+}
+
+tgemm_status_t tgemm_sgemm_lds(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                               const float *B, int64_t ldb, float *C, int64_t ldc, int tile,
+                               int pad, hipStream_t stream)
+{
+    if (!(tile == 2 || tile == 8 || tile == 16 || tile == 32) || !(pad == 0 || pad == 1))
+        return TGEMM_ERROR_NOT_SUPPORTED;
+    Quick quick;
+    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if ((M + tile - 1) / tile > 65535) return TGEMM_ERROR_NOT_SUPPORTED;  // grid rows limit
+    return from_hip(tgemm::launch_lds_tiled(pack(M, N, K, A, lda, B, ldb, C, ldc), tile, pad, stream));
+}
+
+const char *tgemm_status_string(tgemm_status_t status)
+{
+    switch (status) {
+        case TGEMM_SUCCESS: return "success";
+        case TGEMM_ERROR_INVALID_VALUE: return "invalid value (size, leading dimension, pointer or overlap)";
+        case TGEMM_ERROR_NOT_SUPPORTED: return "not supported (size above 2^31-1, alignment, or unknown kernel choice)";
+        case TGEMM_ERROR_HIP: return "HIP runtime refused the launch";
+    }
+    return "unknown status";
+}
+
+int tgemm_version(void) { return 100; }
+
+}  // extern "C"

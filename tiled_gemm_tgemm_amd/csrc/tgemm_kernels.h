@@ -1,0 +1,43 @@
+// Internal interface between the host entry points (api.cpp) and the kernel
+// translation units.  Every launcher takes already-validated arguments:
+// M, N, K >= 1, all sizes below 2^31, leading dimensions large enough, and
+// non-overlapping device buffers.  Each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tgemm {
+
+struct GemmArgs {
+    int M, N, K;
+    const float *A;
+    int64_t lda;
+    const float *B;
+    int64_t ldb;
+    float *C;
+    int64_t ldc;
+};
+
+// One thread per output, 16×16 blocks.
+hipError_t launch_naive(const GemmArgs &g, hipStream_t stream);
+
+// The two-barrier shared-memory tiled kernel; tile in {2, 8, 16, 32}, pad in {0, 1}.
+hipError_t launch_lds_tiled(const GemmArgs &g, int tile, int pad, hipStream_t stream);
+
+// C(i,j) = +0 for i < M, j < N (the empty sum, K = 0).
+hipError_t launch_fill_zero(int M, int N, float *C, int64_t ldc, hipStream_t stream);
+
+// Matrix-core tile configurations.
+struct MfmaVariant {
+    const char *name;
+    int bm, bn, bk;  // macro tile and phase depth
+    int vec;         // 4: 16-byte loads (alignment required), 1: 4-byte loads
+    int wg_per_cu;   // work-groups one compute unit holds at once (LDS bound)
+    hipError_t (*launch)(const GemmArgs &g, hipStream_t stream);
+};
+
+int mfma_variant_count();
+const MfmaVariant *mfma_variant(int index);
+
+}  // namespace tgemm
