@@ -8,7 +8,7 @@ and reported alongside, since the headline metric covers both sizes.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
                   [--kernel auto|naive|lds16|lds32|mfma:<variant>]
-                  [--also NAME,...] [--no-cpu-baseline]
+                  [--also NAME,...] [--no-cpu-baseline] [--copy-bytes N]
 
 Reported:
 * value / ms_per_step — wall clock over the timed steps, between two device
@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="after the timed steps, run one plain device-to-device copy of this many "
+                        "bytes (a known-size reference for hardware byte counters)")
     return p.parse_args()
 
 
@@ -154,18 +157,15 @@ def cpu_baseline(m, target_s: float):
     w = m["workload"]
     A, B = m["A_host"], m["B_host"]
     rows = 2
-    t = 0.0
     while True:
         t0 = time.perf_counter()
         P, S = oracle.gemm_window(A, B, 0, rows, 0, w.N)
         t = time.perf_counter() - t0
         if t >= target_s or rows >= w.M:
             break
-        # scale the sample to the target from the measured rate
-        want = int(rows * min(max(target_s / max(t, 1e-3), 2.0), 64.0))
-        rows = min(w.M, max(rows + 1, want))
-        if t * want / rows > 3 * target_s:
-            break
+        # grow the sample towards the target from the measured rate
+        grow = min(max(1.1 * target_s / max(t, 1e-3), 2.0), 64.0)
+        rows = min(w.M, int(rows * grow))
     macs = rows * w.N * w.K
     C_rows = m["C"][:rows].cpu().numpy().astype(np.float64)
     ok = bool(np.all(np.abs(C_rows - P) <= 4.0 * w.K * 2.0 ** -24 * S))
@@ -241,6 +241,15 @@ def main():
         del ma
     if also:
         line["also"] = also
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_reference_bytes"] = 4 * n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(m, args.cpu_seconds)
     print(json.dumps(line), flush=True)
