@@ -10,6 +10,9 @@ and reported alongside, since the headline metric covers both sizes.
                   [--kernel auto|naive|lds16|lds32|mfma:<variant>]
                   [--also NAME,...] [--no-cpu-baseline] [--copy-bytes N]
 
+Warm-up: at least --warmup calls and at least --warmup-seconds of back-to-back
+calls (the GPU clock takes a few tens of milliseconds of load to settle).
+
 Reported:
 * value / ms_per_step — wall clock over the timed steps, between two device
   synchronisations, throughput = 2·M·N·K / time;
@@ -38,8 +41,8 @@ METRIC = "fp32 GEMM TFLOPS + % of MI355X FP32 matrix peak at 4096³ and 8192³"
 PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/api.cpp",
-                  "tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h"]
+KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/mfma_common.h",
+                  "tiled_gemm_tgemm_amd/csrc/api.cpp", "tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h"]
 
 
 def kernel_source_hash() -> str:
@@ -55,6 +58,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup-seconds", type=float, default=0.5,
+                   help="keep warming up (untimed) until this much time has passed, so the GPU "
+                        "clock has settled before the timed steps")
     p.add_argument("--workload", default="square8192_uniform")
     p.add_argument("--kernel", default="auto")
     p.add_argument("--also", default="square4096_uniform",
@@ -90,7 +96,7 @@ def kernel_call(name: str):
     raise SystemExit(f"unknown --kernel {name}")
 
 
-def time_workload(w, kernel: str, steps: int, warmup: int):
+def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float = 0.0):
     """Time `steps` calls on resident inputs; returns a dict of measurements."""
     import numpy as np
     import torch
@@ -108,8 +114,13 @@ def time_workload(w, kernel: str, steps: int, warmup: int):
         v = tg.tgemm_sgemm_variant_for(w.M, w.N, w.K, A.data_ptr(), w.K, B.data_ptr(), w.N,
                                        C.data_ptr(), w.N)
         variant = tg.tgemm_mfma_variant_name(v)
-    for _ in range(warmup):
+    warm = 0
+    t_warm = time.perf_counter()
+    while warm < warmup or time.perf_counter() - t_warm < warmup_seconds:
         call(A, B, C)
+        warm += 1
+        if warm % 8 == 0:
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()  # the stream every call is queued on
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -126,6 +137,7 @@ def time_workload(w, kernel: str, steps: int, warmup: int):
     kernel_ms = float(per.mean())
     return {
         "workload": w, "A_host": A_h, "B_host": B_h, "C": C, "desc": desc, "variant": variant,
+        "warmup_launches": warm,
         "wall_ms": wall_ms, "kernel_ms": kernel_ms,
         "kernel_ms_min": float(per.min()), "kernel_ms_median": float(np.median(per)),
         "kernel_ms_p90": float(np.percentile(per, 90)),
@@ -196,7 +208,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
 
     w = wl.WORKLOADS[args.workload]
-    m = time_workload(w, args.kernel, args.steps, args.warmup)
+    m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds)
     traffic = traffic_for(w.name, m["desc"]) if args.kernel == "auto" else None
     achieved = m["tflops_kernel"]
     line = {
@@ -206,6 +218,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_launches": m["warmup_launches"],
         "ms_per_step": round(m["wall_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -228,7 +241,7 @@ def main():
     also = {}
     for name in [x for x in args.also.split(",") if x and x != w.name]:
         wa = wl.WORKLOADS[name]
-        ma = time_workload(wa, args.kernel, args.steps, args.warmup)
+        ma = time_workload(wa, args.kernel, args.steps, args.warmup, args.warmup_seconds)
         also[name] = {
             "tflops": round(ma["tflops_wall"], 3),
             "ms_per_step": round(ma["wall_ms"], 4),

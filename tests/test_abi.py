@@ -60,7 +60,7 @@ def test_static_queries(lib):
     n = tg.tgemm_mfma_variant_count()
     assert n >= 6
     names = tg.variant_names()
-    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_w\dx\d_vec[14]", x) for x in names)
+    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_w\dx\d_vec[14](_flat)?", x) for x in names)
     assert tg.tgemm_mfma_variant_name(n) is None and tg.tgemm_mfma_variant_name(-1) is None
     for st in range(4):
         assert tg.tgemm_status_string(st)
@@ -117,6 +117,13 @@ def test_kernel_choice_checks(lib):
         assert tg.tgemm_sgemm_lds(*args, tile, pad, None) == UNSUPPORTED
     # a 16-byte-load variant on operands that cannot take them
     vec4 = [i for i, name in enumerate(tg.variant_names()) if name.endswith("vec4")]
+    # buffer-load configurations refuse leading dimensions beyond 32-bit offsets
+    buf = [i for i, name in enumerate(tg.variant_names()) if not name.endswith("_flat")]
+    flat = [i for i, name in enumerate(tg.variant_names()) if name.endswith("_flat")]
+    assert flat and buf
+    for v in buf:
+        assert tg.tgemm_sgemm_mfma(64, 64, 64, 1 << 40, 1 << 24, 1 << 44, 64, 1 << 46, 64, v,
+                                   None) == UNSUPPORTED
     assert tg.tgemm_sgemm_mfma(64, 63, 64, A_, 64, B_, 63, C_, 63, vec4[0], None) == UNSUPPORTED
     assert tg.tgemm_sgemm_mfma(64, 64, 63, A_, 63, B_, 64, C_, 64, vec4[0], None) == UNSUPPORTED
     assert tg.tgemm_sgemm_mfma(64, 64, 64, A_ + 4, 64, B_, 64, C_, 64, vec4[0], None) == UNSUPPORTED
@@ -125,16 +132,20 @@ def test_kernel_choice_checks(lib):
 def test_variant_choice(lib):
     names = tg.variant_names()
 
-    def chosen(M, N, K, a=A_, lda=None, ldb=None, ldc=None):
-        v = tg.tgemm_sgemm_variant_for(M, N, K, a, lda or K, B_, ldb or N, C_, ldc or N)
+    def chosen(M, N, K, a=1 << 40, lda=None, ldb=None, ldc=None):
+        v = tg.tgemm_sgemm_variant_for(M, N, K, a, lda or K, 1 << 44, ldb or N, 1 << 46, ldc or N)
         return names[v] if v >= 0 else None
 
-    assert chosen(8192, 8192, 8192) == "m256n256k32_w2x2_vec4"
-    assert chosen(4096, 4096, 4096) == "m256n256k32_w2x2_vec4"
+    assert chosen(8192, 8192, 8192) == "m256n128k16_w2x2_vec4"
+    assert chosen(4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
+    assert chosen(3000, 5000, 1000) == "m256n128k16_w2x2_vec4"
+    assert chosen(512, 512, 512) == "m64n64k32_w2x2_vec4"
+    assert chosen(1024, 1024, 1024) == "m64n64k32_w2x2_vec4"
+    assert chosen(300, 300, 300, lda=1 << 24).endswith("_flat")   # lda beyond 32-bit offsets
     assert chosen(512, 512, 512).endswith("vec4")
     assert chosen(1024, 1024, 1024).endswith("vec4")
     assert chosen(3000, 5000, 1000).endswith("vec4")
     assert chosen(7, 5, 3).endswith("vec1")          # K, N not multiples of 4
-    assert chosen(64, 64, 64, a=A_ + 4).endswith("vec1")  # A not 16-byte aligned
+    assert chosen(64, 64, 64, a=(1 << 40) + 4).endswith("vec1")  # A not 16-byte aligned
     assert chosen(0, 4, 4) is None and chosen(4, 4, 0) is None
-    assert tg.tgemm_sgemm_variant_for(4, 4, 4, A_, 2, B_, 4, C_, 4) == -1
+    assert tg.tgemm_sgemm_variant_for(4, 4, 4, A_, 2, B_, 4, C_, 4) == -1  # lda < K

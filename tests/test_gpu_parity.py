@@ -100,6 +100,11 @@ def vec4_shape(M, N, K):
     return K % 4 == 0 and N % 4 == 0
 
 
+def runnable(name, M, N, K):
+    """Whether variant `name` takes contiguous aligned M×K·K×N operands."""
+    return not name.endswith("vec4") and not name.endswith("vec4_flat") or vec4_shape(M, N, K)
+
+
 def auto_variant(M, N, K):
     """Name of the variant tgemm_sgemm picks for contiguous, aligned operands."""
     v = tg.tgemm_sgemm_variant_for(M, N, K, 1 << 20, K, 1 << 36, N, 1 << 44, N)
@@ -213,7 +218,7 @@ def test_edge_shapes_integer_exact(M, N, K):
     log(f"edge {M}x{N}x{K}")
     assert_exact(run(A, B), Pi, "auto")
     for v, name in enumerate(variants()):
-        if name.endswith("vec4") and not vec4_shape(M, N, K):
+        if not runnable(name, M, N, K):
             continue
         assert_exact(run(A, B, "mfma", variant=v), Pi, name)
     assert_exact(run(A, B, "naive"), Pi, "naive")
@@ -247,7 +252,7 @@ def test_guard_bands(M, N, K, pad):
     A, B = int_inputs(M, N, K, 5 + M + N + K)
     Pi = oracle.gemm_i64(A, B)
     kernels = [("auto", {})] + [("mfma", {"variant": v}) for v, n in enumerate(variants())
-                                if not (n.endswith("vec4") and (pad % 4 or not vec4_shape(M, N, K)))]
+                                if runnable(n, M, N, K) and ("vec1" in n or pad % 4 == 0)]
     kernels += [("naive", {}), ("lds", {"tile": 16, "pad": 1})]
     for kernel, kw in kernels:
         log(f"guard {M}x{N}x{K} pad {pad}: {kernel} {kw}")
@@ -263,6 +268,43 @@ def test_guard_bands(M, N, K, pad):
         assert np.all(big[outside] == 12345.0), f"{kernel} {kw} wrote outside C"
 
 
+@pytest.mark.parametrize("K", [1, 4, 15, 16, 17, 20, 31, 32, 33, 36, 48, 64, 100])
+def test_partial_phases_integer_exact(K):
+    """K below, at and just past the phase depths (16 and 32) of every
+    configuration, with ragged M and N, in integers (exact)."""
+    M, N = 259, 131 if K % 4 else 132
+    A, B = int_inputs(M, N, K, 1000 + K)
+    Pi = oracle.gemm_i64(A, B)
+    log(f"partial phases K={K}")
+    for v, name in enumerate(variants()):
+        if runnable(name, M, N, K):
+            assert_exact(run(A, B, "mfma", variant=v), Pi, f"{name} K={K}")
+    assert_exact(run(A, B), Pi, "auto")
+
+
+def test_leading_dimension_beyond_buffer_offsets():
+    """lda past what 32-bit buffer offsets cover: tgemm_sgemm runs the 64-bit
+    pointer configuration, buffer configurations refuse it."""
+    M, N, K = 130, 68, 40
+    lda = (1 << 23) + 8  # past every buffer configuration's limit (BM rows × lda × 4 B < 2^31)
+    A, B = int_inputs(M, N, K, 4242)
+    Pi = oracle.gemm_i64(A, B)
+    big = torch.empty((M, lda), dtype=torch.float32, device="cuda")
+    big[:, :K] = dev(A)
+    Av = big[:, :K]
+    dB = dev(B)
+    C = tg.sgemm(Av, dB)
+    torch.cuda.synchronize()
+    assert_exact(C.cpu().numpy(), Pi, "auto, huge lda")
+    v = tg.tgemm_sgemm_variant_for(M, N, K, Av.data_ptr(), lda, dB.data_ptr(), N, C.data_ptr(), N)
+    assert variants()[v].endswith("_flat")
+    for v, name in enumerate(variants()):
+        st = tg.tgemm_sgemm_mfma(M, N, K, Av.data_ptr(), lda, dB.data_ptr(), N, C.data_ptr(), N, v, None)
+        assert (st == tg.TGEMM_SUCCESS) == name.endswith("_flat"), name
+    torch.cuda.synchronize()
+    del big
+
+
 # ------------------------------------------------------------ identities and invariants
 
 def test_identities_bit_exact_real_inputs():
@@ -272,7 +314,7 @@ def test_identities_bit_exact_real_inputs():
     for (M, N, K) in [(200, 136, 72), (64, 64, 64), (33, 65, 129)]:
         A, B, _ = wl.random_matrices(M, N, K, "normal", 31)
         for kernel, kw in [("auto", {})] + [("mfma", {"variant": v}) for v, n in enumerate(variants())
-                                             if not (n.endswith("vec4") and not vec4_shape(M, N, K))]:
+                                             if runnable(n, M, N, K)]:
             log(f"identities {M}x{N}x{K} {kernel} {kw}")
             assert np.array_equal(run(np.eye(M, dtype=np.float32), A, kernel, **kw), A)
             assert np.array_equal(run(B, np.eye(N, dtype=np.float32), kernel, **kw), B)
@@ -294,7 +336,7 @@ def test_one_hot_locates_every_position():
         want = np.zeros((M, N), np.float32)
         want[i0, j0] = -15.0
         for v, name in enumerate(variants()):
-            if name.endswith("vec4") and not vec4_shape(M, N, K):
+            if not runnable(name, M, N, K):
                 continue
             assert np.array_equal(run(A, B, "mfma", variant=v), want), (name, i0, k0, j0)
 

@@ -80,12 +80,20 @@ bool vec4_ok(int64_t N, int64_t K, const float *A, int64_t lda, const float *B, 
            ldc % 4 == 0 && K % 4 == 0 && N % 4 == 0;
 }
 
-// Estimated cost of a configuration in units of one phase of one 64×64
-// wavefront sub-tile of matrix-core work on one SIMD.  Work-groups are dealt
+// Whether a configuration can run these operands: 16-byte loads need
+// vec4_ok, and buffer-load configurations bound the leading dimensions.
+bool runs(const tgemm::MfmaVariant &v, bool vec4, int64_t lda, int64_t ldb)
+{
+    return (v.vec == 1 || vec4) && lda <= v.max_lda && ldb <= v.max_ldb;
+}
+
+// Estimated time of a configuration in SIMD cycles.  Work-groups are dealt
 // to the 256 compute units in rounds; in a round each CU holds `resident`
-// work-groups (at most what its LDS allows) whose 4 wavefronts share its 4
-// SIMDs.  Edge tiles cost as much as full ones, which is what makes smaller
-// tiles win on small or ragged shapes.
+// work-groups (at most what its LDS and registers allow) whose 4 wavefronts
+// share its 4 SIMDs, each SIMD retiring 64 flops per cycle at the
+// configuration's measured efficiency.  Edge tiles cost as much as full
+// ones, which is what makes smaller tiles win on small or ragged shapes; a
+// fixed cost per round stands for the first load and the C stores.
 double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
 {
     const int64_t cus = 256;
@@ -93,22 +101,20 @@ double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
     int64_t resident = (tiles + cus - 1) / cus;
     if (resident > v.wg_per_cu) resident = v.wg_per_cu;
     const int64_t rounds = (tiles + cus * resident - 1) / (cus * resident);
-    const int64_t phases = (K + v.bk - 1) / v.bk;
-    const double per_round = (double)phases * ((double)v.bm * v.bn / (64.0 * 64.0)) / 4.0 * resident;
-    // fixed cost per phase (barrier, LDS latency) and per work-group
-    const double overhead = (double)phases * 0.5 + 2.0;
-    return (double)rounds * (per_round + overhead);
+    const double kpad = (double)((K + v.bk - 1) / v.bk) * v.bk;
+    const double per_wg = 2.0 * v.bm * v.bn * kpad / 4.0 / 64.0 / v.efficiency;
+    return (double)rounds * ((double)resident * per_wg + 3000.0);
 }
 
 int choose_variant(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                    int64_t ldb, const float *C, int64_t ldc)
 {
-    const int vec = vec4_ok(N, K, A, lda, B, ldb, C, ldc) ? 4 : 1;
+    const bool vec4 = vec4_ok(N, K, A, lda, B, ldb, C, ldc);
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
-        if (v->vec != vec) continue;
+        if (!runs(*v, vec4, lda, ldb)) continue;
         const double c = cost(*v, M, N, K);
         if (best < 0 || c < best_cost) {
             best = i;
@@ -132,7 +138,7 @@ tgemm_status_t tgemm_sgemm_mfma(int64_t M, int64_t N, int64_t K, const float *A,
     const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
     if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
-    if (v->vec == 4 && !vec4_ok(N, K, A, lda, B, ldb, C, ldc)) return TGEMM_ERROR_NOT_SUPPORTED;
+    if (!runs(*v, vec4_ok(N, K, A, lda, B, ldb, C, ldc), lda, ldb)) return TGEMM_ERROR_NOT_SUPPORTED;
     return from_hip(v->launch(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
 }
 

@@ -31,13 +31,29 @@ hipError_t launch_fill_zero(int M, int N, float *C, int64_t ldc, hipStream_t str
 // Matrix-core tile configurations.
 struct MfmaVariant {
     const char *name;
-    int bm, bn, bk;  // macro tile and phase depth
-    int vec;         // 4: 16-byte loads (alignment required), 1: 4-byte loads
-    int wg_per_cu;   // work-groups one compute unit holds at once (LDS bound)
+    int bm, bn, bk;      // macro tile and phase depth
+    int vec;             // 4: 16-byte loads (alignment required), 1: 4-byte loads
+    int wg_per_cu;       // work-groups one compute unit holds at once
+    int64_t max_lda;     // largest leading dimensions the configuration takes
+    int64_t max_ldb;
+    double efficiency;   // measured fraction of the matrix-core peak at large sizes
     hipError_t (*launch)(const GemmArgs &g, hipStream_t stream);
 };
 
-int mfma_variant_count();
-const MfmaVariant *mfma_variant(int index);
+// Buffer-load kernels (mfma_sgemm.hip) and the 64-bit-pointer fallback
+// (mfma_sgemm_flat.hip).
+int mfma_buffer_variant_count();
+const MfmaVariant *mfma_buffer_variant(int index);
+int mfma_flat_variant_count();
+const MfmaVariant *mfma_flat_variant(int index);
+
+// All configurations, buffer-load ones first.
+inline int mfma_variant_count() { return mfma_buffer_variant_count() + mfma_flat_variant_count(); }
+inline const MfmaVariant *mfma_variant(int index)
+{
+    if (index < 0) return nullptr;
+    if (index < mfma_buffer_variant_count()) return mfma_buffer_variant(index);
+    return mfma_flat_variant(index - mfma_buffer_variant_count());
+}
 
 }  // namespace tgemm
