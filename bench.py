@@ -42,6 +42,7 @@ PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/mfma_common.h",
+                  "tiled_gemm_tgemm_amd/csrc/mfma_sgemm_small.hip",
                   "tiled_gemm_tgemm_amd/csrc/api.cpp", "tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h"]
 
 

@@ -286,7 +286,7 @@ def test_leading_dimension_beyond_buffer_offsets():
     """lda past what 32-bit buffer offsets cover: tgemm_sgemm runs the 64-bit
     pointer configuration, buffer configurations refuse it."""
     M, N, K = 130, 68, 40
-    lda = (1 << 23) + 8  # past every buffer configuration's limit (BM rows × lda × 4 B < 2^31)
+    lda = (1 << 24) + 8  # past every buffer configuration's limit (32+ rows × lda × 4 B >= 2^31)
     A, B = int_inputs(M, N, K, 4242)
     Pi = oracle.gemm_i64(A, B)
     big = torch.empty((M, lda), dtype=torch.float32, device="cuda")

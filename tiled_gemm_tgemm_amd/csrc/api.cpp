@@ -88,22 +88,31 @@ bool runs(const tgemm::MfmaVariant &v, bool vec4, int64_t lda, int64_t ldb)
 }
 
 // Estimated time of a configuration in SIMD cycles.  Work-groups are dealt
-// to the 256 compute units in rounds; in a round each CU holds `resident`
-// work-groups (at most what its LDS and registers allow) whose 4 wavefronts
-// share its 4 SIMDs, each SIMD retiring 64 flops per cycle at the
-// configuration's measured efficiency.  Edge tiles cost as much as full
-// ones, which is what makes smaller tiles win on small or ragged shapes; a
-// fixed cost per round stands for the first load and the C stores.
+// to the 256 compute units in rounds of up to wg_per_cu per CU; the
+// wavefronts of a work-group spread over the CU's 4 SIMDs, each retiring 64
+// flops a cycle at the efficiency measured for that many resident
+// work-groups (interpolated between alone and full).  The last round may
+// leave CUs less full, and is costed at its own residency.  Edge tiles cost
+// as much as full ones, which is what makes smaller tiles win on small or
+// ragged shapes.
 double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
 {
     const int64_t cus = 256;
     const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
-    int64_t resident = (tiles + cus - 1) / cus;
-    if (resident > v.wg_per_cu) resident = v.wg_per_cu;
-    const int64_t rounds = (tiles + cus * resident - 1) / (cus * resident);
+    const int64_t full_rounds = tiles / (cus * v.wg_per_cu);
+    const int64_t rest = tiles % (cus * v.wg_per_cu);
     const double kpad = (double)((K + v.bk - 1) / v.bk) * v.bk;
-    const double per_wg = 2.0 * v.bm * v.bn * kpad / 4.0 / 64.0 / v.efficiency;
-    return (double)rounds * ((double)resident * per_wg + 3000.0);
+    const double per_wg = 2.0 * v.bm * v.bn * kpad / 4.0 / 64.0;
+    auto eff = [&](int64_t r) {
+        if (v.wg_per_cu <= 1) return v.eff_full;
+        return v.eff_alone + (v.eff_full - v.eff_alone) * (double)(r - 1) / (double)(v.wg_per_cu - 1);
+    };
+    double t = (double)full_rounds * ((double)v.wg_per_cu * per_wg / eff(v.wg_per_cu) + v.round_cycles);
+    if (rest > 0) {
+        const int64_t r = (rest + cus - 1) / cus;
+        t += (double)r * per_wg / eff(r) + v.round_cycles;
+    }
+    return t;
 }
 
 int choose_variant(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,

@@ -38,23 +38,24 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int group_m, i
     tn = in_group / rows;
 }
 
-// One wavefront's view of a phase held in LDS: As[m][k] with row stride AS
-// words, Bs[k][n] with row stride BS words.  In step s of k-group g the lanes
-// of half h feed k = 8g + 4h + s to both operands, so a lane's four A values
-// of a group are adjacent and come in one 16-byte read.
-template <int FM, int FN, int AS, int BS>
+// One wavefront's view of a phase held in LDS: As holds the BM×BK slice of A
+// (row-major, layout chosen by the kernel), Bs[k][n] the BK×BN slice of B
+// with row stride BS words.  In step s of k-group g the lanes of half h feed
+// k = 8g + 4h + s to both operands, so a lane's four A values of a group are
+// adjacent and come in one 16-byte read.
+template <int FM, int FN, int BS>
 struct Fragments {
     f32x4 a[FM];
     float b[FN][4];
 
-    // a_frag = offset of (row wm*TM + l32, column 4*half) in As;
-    // b_frag = offset of (row 4*half, column wn*TN + l32) in Bs.
-    __device__ __forceinline__ void read(const float *as, const float *bs, int a_frag, int b_frag,
-                                         int g)
+    // a_off[i]: word offset in As of (row wm*TM + 32i + l32, columns 8g+4h ..
+    // 8g+4h+3) for this group g; b_frag: offset of (row 4h, column
+    // wn*TN + l32) in Bs.
+    __device__ __forceinline__ void read(const float *as, const float *bs, const int (&a_off)[FM],
+                                         int b_frag, int g)
     {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            a[i] = *reinterpret_cast<const f32x4 *>(as + a_frag + i * 32 * AS + 8 * g);
+        for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const f32x4 *>(as + a_off[i]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -77,15 +78,15 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[FM][FN], const Frag &f)
 
 // A whole phase of BK values of k from one LDS stage; the reads of group
 // g+1 are issued before the matrix-core steps of group g.
-template <int FM, int FN, int AS, int BS, int BK>
+template <int FM, int FN, int BS, int BK>
 __device__ __forceinline__ void mfma_phase(f32x16 (&acc)[FM][FN], const float *as, const float *bs,
-                                           int a_frag, int b_frag)
+                                           const int (&a_off)[BK / 8][FM], int b_frag)
 {
-    Fragments<FM, FN, AS, BS> f[2];
-    f[0].read(as, bs, a_frag, b_frag, 0);
+    Fragments<FM, FN, BS> f[2];
+    f[0].read(as, bs, a_off[0], b_frag, 0);
 #pragma unroll
     for (int g = 0; g < BK / 8; ++g) {
-        if (g + 1 < BK / 8) f[(g + 1) & 1].read(as, bs, a_frag, b_frag, g + 1);
+        if (g + 1 < BK / 8) f[(g + 1) & 1].read(as, bs, a_off[g + 1], b_frag, g + 1);
         mfma_group<FM, FN>(acc, f[g & 1]);
     }
 }

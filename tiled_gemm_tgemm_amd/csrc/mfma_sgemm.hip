@@ -172,12 +172,15 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
             b_reg[i] = Vec<VEC>::load(rb, off);
         }
     };
-    float *a_st = lds + a_r0 * G::AS + a_c;
+    // LDS word offset of each A slot in a stage
+    int a_st[G::LA];
+#pragma unroll
+    for (int i = 0; i < G::LA; ++i) a_st[i] = (a_r0 + i * G::RA) * G::AS + a_c;
     float *b_st = lds + G::A_STAGE + b_r0 * G::BS + b_c;
     auto store_phase = [&] __device__(int stage) {
 #pragma unroll
         for (int i = 0; i < G::LA; ++i)
-            *reinterpret_cast<vec_t *>(a_st + stage * G::STAGE + i * G::RA * G::AS) = a_reg[i];
+            *reinterpret_cast<vec_t *>(lds + stage * G::STAGE + a_st[i]) = a_reg[i];
 #pragma unroll
         for (int i = 0; i < G::LB; ++i)
             *reinterpret_cast<vec_t *>(b_st + stage * G::STAGE + i * G::RB * G::BS) = b_reg[i];
@@ -189,11 +192,15 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-    const int a_frag = (wm * G::TM + l32) * G::AS + 4 * half;
+    int a_frag[G::BK / 8][G::FM];
+#pragma unroll
+    for (int g = 0; g < G::BK / 8; ++g)
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i) a_frag[g][i] = (wm * G::TM + i * 32 + l32) * G::AS + 8 * g + 4 * half;
     const int b_frag = (4 * half) * G::BS + wn * G::TN + l32;
     auto compute = [&] __device__(int stage) {
         const float *as = lds + stage * G::STAGE;
-        mfma::mfma_phase<G::FM, G::FN, G::AS, G::BS, G::BK>(acc, as, as + G::A_STAGE, a_frag, b_frag);
+        mfma::mfma_phase<G::FM, G::FN, G::BS, G::BK>(acc, as, as + G::A_STAGE, a_frag, b_frag);
     };
 
     const int full = K / G::BK;            // phases with all BK values of k
@@ -262,21 +269,20 @@ constexpr int64_t max_ldb()
     return ((((int64_t)1 << 31) - 16) / 4 - G::BN) / G::BK;
 }
 
-#define TGEMM_VARIANT(name, G, eff)                                                          \
-    {                                                                                         \
-        name, G::BM, G::BN, G::BK, G::VEC, wg_per_cu<G>(), max_lda<G>(), max_ldb<G>(), eff, \
-            &launch_cfg<G>                                                                    \
+#define TGEMM_VARIANT(name, G, alone, full)                                                    \
+    {                                                                                           \
+        name, G::BM, G::BN, G::BK, G::VEC, wg_per_cu<G>(), max_lda<G>(), max_ldb<G>(), alone, \
+            full, 7000.0, &launch_cfg<G>                                                        \
     }
 
-// eff: measured steady-state fraction of the matrix-core peak at large
-// sizes, used only to rank configurations.
+// Efficiencies measured on MI355X (square and ragged shapes from 512 to 8192).
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.91),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.89),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.80),
-    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.70),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.68),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.60),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.70, 0.91),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.68, 0.88),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.49, 0.77),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.66, 0.86),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.64, 0.84),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.47, 0.74),
 };
 
 }  // namespace

@@ -127,7 +127,11 @@ void mfma_sgemm_flat_kernel(int M, int N, int K, const float *__restrict__ A, in
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-    const int a_frag = (wm * G::TM + l32) * G::AS + 4 * half;
+    int a_off[G::BK / 8][G::FM];
+#pragma unroll
+    for (int g = 0; g < G::BK / 8; ++g)
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i) a_off[g][i] = (wm * G::TM + i * 32 + l32) * G::AS + 8 * g + 4 * half;
     const int b_frag = (4 * half) * G::BS + wn * G::TN + l32;
     const int phases = (K + G::BK - 1) / G::BK;
     load_phase(0);
@@ -137,7 +141,7 @@ void mfma_sgemm_flat_kernel(int M, int N, int K, const float *__restrict__ A, in
         const bool more = p + 1 < phases;
         if (more) load_phase((p + 1) * G::BK);
         const float *as = lds + (p & 1) * G::STAGE;
-        mfma::mfma_phase<G::FM, G::FN, G::AS, G::BS, G::BK>(acc, as, as + G::A_STAGE, a_frag, b_frag);
+        mfma::mfma_phase<G::FM, G::FN, G::BS, G::BK>(acc, as, as + G::A_STAGE, a_off, b_frag);
         if (more) store_phase((p + 1) & 1, (p + 1) * G::BK);
         __syncthreads();
     }
@@ -163,8 +167,8 @@ typedef FlatCfg<128, 128, 32, 2, 2, 4, 8, 2> Flat4;
 typedef FlatCfg<128, 128, 32, 2, 2, 1, 8, 2> Flat1;
 
 const MfmaVariant kFlatVariants[] = {
-    {"m128n128k32_w2x2_vec4_flat", 128, 128, 32, 4, 2, INT64_MAX, INT64_MAX, 0.80, &launch_flat<Flat4>},
-    {"m128n128k32_w2x2_vec1_flat", 128, 128, 32, 1, 2, INT64_MAX, INT64_MAX, 0.60, &launch_flat<Flat1>},
+    {"m128n128k32_w2x2_vec4_flat", 128, 128, 32, 4, 2, INT64_MAX, INT64_MAX, 0.55, 0.75, 7000.0, &launch_flat<Flat4>},
+    {"m128n128k32_w2x2_vec1_flat", 128, 128, 32, 1, 2, INT64_MAX, INT64_MAX, 0.45, 0.60, 7000.0, &launch_flat<Flat1>},
 };
 
 }  // namespace

@@ -36,24 +36,35 @@ struct MfmaVariant {
     int wg_per_cu;       // work-groups one compute unit holds at once
     int64_t max_lda;     // largest leading dimensions the configuration takes
     int64_t max_ldb;
-    double efficiency;   // measured fraction of the matrix-core peak at large sizes
+    // Measured fraction of the matrix-core rate a work-group sustains when it
+    // is alone on its compute unit, and when wg_per_cu of them share it; plus
+    // a fixed cost per round of work-groups (SIMD cycles).  Used only to rank
+    // configurations for a shape.
+    double eff_alone, eff_full, round_cycles;
     hipError_t (*launch)(const GemmArgs &g, hipStream_t stream);
 };
 
-// Buffer-load kernels (mfma_sgemm.hip) and the 64-bit-pointer fallback
-// (mfma_sgemm_flat.hip).
+// Tiled buffer-load kernels (mfma_sgemm.hip), the small-product kernel
+// (mfma_sgemm_small.hip) and the 64-bit-pointer fallback (mfma_sgemm_flat.hip).
 int mfma_buffer_variant_count();
 const MfmaVariant *mfma_buffer_variant(int index);
+int mfma_small_variant_count();
+const MfmaVariant *mfma_small_variant(int index);
 int mfma_flat_variant_count();
 const MfmaVariant *mfma_flat_variant(int index);
 
-// All configurations, buffer-load ones first.
-inline int mfma_variant_count() { return mfma_buffer_variant_count() + mfma_flat_variant_count(); }
+// All configurations, in that order.
+inline int mfma_variant_count()
+{
+    return mfma_buffer_variant_count() + mfma_small_variant_count() + mfma_flat_variant_count();
+}
 inline const MfmaVariant *mfma_variant(int index)
 {
     if (index < 0) return nullptr;
     if (index < mfma_buffer_variant_count()) return mfma_buffer_variant(index);
-    return mfma_flat_variant(index - mfma_buffer_variant_count());
+    index -= mfma_buffer_variant_count();
+    if (index < mfma_small_variant_count()) return mfma_small_variant(index);
+    return mfma_flat_variant(index - mfma_small_variant_count());
 }
 
 }  // namespace tgemm
