@@ -69,6 +69,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--op-a", choices=("N", "T"), default="N",
+                   help="T: A is stored transposed (K×M) and passed as TGEMM_OP_T")
+    p.add_argument("--op-b", choices=("N", "T"), default="N",
+                   help="T: B is stored transposed (N×K) and passed as TGEMM_OP_T")
+    p.add_argument("--cold", action="store_true",
+                   help="before every timed call, overwrite a 512 MiB buffer so that L2 and the "
+                        "256 MB Infinity Cache hold none of the operands (kernel time only)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed steps, run one plain device-to-device copy of this many "
                         "bytes (a known-size reference for hardware byte counters)")
@@ -97,7 +104,8 @@ def kernel_call(name: str):
     raise SystemExit(f"unknown --kernel {name}")
 
 
-def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float = 0.0):
+def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float = 0.0,
+                  cold: bool = False, op_a: str = "N", op_b: str = "N"):
     """Time `steps` calls on resident inputs; returns a dict of measurements."""
     import numpy as np
     import torch
@@ -106,15 +114,19 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
     from tiled_gemm_tgemm_amd import workloads as wl
 
     A_h, B_h = wl.make_inputs(w)
-    A = torch.from_numpy(A_h).cuda()
-    B = torch.from_numpy(B_h).cuda()
+    # a transposed operand is stored transposed and handed over as a view
+    A = torch.from_numpy(np.ascontiguousarray(A_h.T)).cuda().t() if op_a == "T" else torch.from_numpy(A_h).cuda()
+    B = torch.from_numpy(np.ascontiguousarray(B_h.T)).cuda().t() if op_b == "T" else torch.from_numpy(B_h).cuda()
     C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
     call, desc = kernel_call(kernel)
     variant = None
     if kernel == "auto":
-        v = tg.tgemm_sgemm_variant_for(w.M, w.N, w.K, A.data_ptr(), w.K, B.data_ptr(), w.N,
-                                       C.data_ptr(), w.N)
+        ops = (tg.TGEMM_OP_T if op_a == "T" else tg.TGEMM_OP_N, tg.TGEMM_OP_T if op_b == "T" else tg.TGEMM_OP_N)
+        v = tg.tgemm_sgemm_variant_for_ex(*ops, w.M, w.N, w.K, A.data_ptr(), w.M if op_a == "T" else w.K,
+                                          B.data_ptr(), w.K if op_b == "T" else w.N, C.data_ptr(), w.N)
         variant = tg.tgemm_mfma_variant_name(v)
+        if op_a == "T" or op_b == "T":
+            desc = f"tgemm_sgemm_ex(op_a={op_a},op_b={op_b})"
     warm = 0
     t_warm = time.perf_counter()
     while warm < warmup or time.perf_counter() - t_warm < warmup_seconds:
@@ -126,15 +138,19 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if cold else None
     t0 = time.perf_counter()
     for i in range(steps):
+        if cold:
+            flush.fill_(float(i))
         starts[i].record(stream)
         call(A, B, C)
         ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
-    wall_ms = (t1 - t0) * 1e3 / steps
+    # with --cold the wall clock also covers the flushes: report kernel time only
+    wall_ms = float(per.mean()) if cold else (t1 - t0) * 1e3 / steps
     kernel_ms = float(per.mean())
     return {
         "workload": w, "A_host": A_h, "B_host": B_h, "C": C, "desc": desc, "variant": variant,
@@ -209,8 +225,10 @@ def main():
     props = torch.cuda.get_device_properties(0)
 
     w = wl.WORKLOADS[args.workload]
-    m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds)
-    traffic = traffic_for(w.name, m["desc"]) if args.kernel == "auto" else None
+    m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,
+                      args.op_a, args.op_b)
+    plain = args.kernel == "auto" and args.op_a == "N" and args.op_b == "N" and not args.cold
+    traffic = traffic_for(w.name, m["desc"]) if plain else None
     achieved = m["tflops_kernel"]
     line = {
         "metric": METRIC,
@@ -226,8 +244,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "caches": "cold (512 MiB flush before each call; kernel time)" if args.cold else "warm",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "values": w.dist,
-                   "seed": w.seed, "kernel": m["desc"], "variant": m["variant"]},
+                   "seed": w.seed, "kernel": m["desc"], "variant": m["variant"],
+                   "op_a": args.op_a, "op_b": args.op_b},
         "pct_of_fp32_matrix_peak": round(100.0 * m["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2),
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MATRIX_TFLOPS,
@@ -242,7 +262,8 @@ def main():
     also = {}
     for name in [x for x in args.also.split(",") if x and x != w.name]:
         wa = wl.WORKLOADS[name]
-        ma = time_workload(wa, args.kernel, args.steps, args.warmup, args.warmup_seconds)
+        ma = time_workload(wa, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,
+                           args.op_a, args.op_b)
         also[name] = {
             "tflops": round(ma["tflops_wall"], 3),
             "ms_per_step": round(ma["wall_ms"], 4),

@@ -52,6 +52,12 @@ extern "C" {
 /* Same definition as the HIP runtime's, so either header may come first. */
 typedef struct ihipStream_t *hipStream_t;
 
+/* How an operand is stored (BLAS's "op"): as is, or transposed. */
+typedef enum tgemm_op {
+    TGEMM_OP_N = 0, /* op(X) = X */
+    TGEMM_OP_T = 1  /* op(X) = Xᵀ */
+} tgemm_op_t;
+
 typedef enum tgemm_status {
     TGEMM_SUCCESS = 0,
     TGEMM_ERROR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer or overlap */
@@ -73,23 +79,51 @@ tgemm_status_t tgemm_sgemm(int64_t M, int64_t N, int64_t K,
                            float *C, int64_t ldc, hipStream_t stream);
 
 /*
+ * C = op(A)·op(B), op(A) M×K and op(B) K×N, with the tiled matrix-core kernel.
+ * op_a = TGEMM_OP_T: A is stored K×M row-major (op(A) = Aᵀ), op(A)(i,k) =
+ * A[k*lda + i], lda >= max(1,M); otherwise as tgemm_sgemm.  op_b = TGEMM_OP_T:
+ * B is stored N×K, op(B)(k,j) = B[j*ldb + k], ldb >= max(1,K).  Each operand
+ * is read along the dimension it is contiguous in and kept that way on chip,
+ * the fragments taking whichever order the matrix cores need (page 1,
+ * section [Coalescing], "Corner Turning").  Other values of op_a / op_b:
+ * TGEMM_ERROR_NOT_SUPPORTED.  Transposed operands need leading dimensions
+ * below 2^21 (the 64-bit-pointer configuration takes operands as stored
+ * only): otherwise TGEMM_ERROR_NOT_SUPPORTED.  tgemm_sgemm(...) is
+ * tgemm_sgemm_ex(TGEMM_OP_N, TGEMM_OP_N, ...).
+ */
+tgemm_status_t tgemm_sgemm_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                              const float *A, int64_t lda,
+                              const float *B, int64_t ldb,
+                              float *C, int64_t ldc, hipStream_t stream);
+
+/*
  * Same product with an explicitly chosen matrix-core tile configuration,
- * 0 <= variant < tgemm_mfma_variant_count().  Variants whose vector loads
- * need 16-byte alignment return TGEMM_ERROR_NOT_SUPPORTED when A, B, C,
- * lda, ldb, ldc, K or N do not allow them (see tgemm_mfma_variant_name).
+ * 0 <= variant < tgemm_mfma_variant_count().  Variants with 16-byte loads
+ * ("vec4") need A and B 16-byte aligned, lda, ldb and the stored row lengths
+ * of A and B (K and N here) multiples of 4; buffer-load variants need their
+ * 32-bit offsets to span the leading dimensions; otherwise, and for an
+ * unknown variant, TGEMM_ERROR_NOT_SUPPORTED.
  */
 tgemm_status_t tgemm_sgemm_mfma(int64_t M, int64_t N, int64_t K,
                                 const float *A, int64_t lda,
                                 const float *B, int64_t ldb,
                                 float *C, int64_t ldc, int variant, hipStream_t stream);
 
+/* tgemm_sgemm_mfma with operand orders, as tgemm_sgemm_ex. */
+tgemm_status_t tgemm_sgemm_mfma_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                                   const float *A, int64_t lda,
+                                   const float *B, int64_t ldb,
+                                   float *C, int64_t ldc, int variant, hipStream_t stream);
+
 /* Number of matrix-core tile configurations. */
 int tgemm_mfma_variant_count(void);
 
 /*
- * Static description of a variant, e.g. "m256n256k32_w2x2_vec4"
- * (macro tile 256×256, depth 32 per phase, 2×2 wavefronts, 16-byte loads);
- * NULL for an index out of range.
+ * Static description of a variant, e.g. "m256n128k16_w2x2_vec4" (macro tile
+ * 256×128, depth 16 per phase, 2×2 wavefronts, 16-byte loads),
+ * "m32n32k8_s4d4_vec4" (32×32 tile, K split over 4 wavefronts, 4 groups of 8
+ * in flight), "..._flat" (64-bit pointers, any leading dimension, operands
+ * as stored only); NULL for an index out of range.
  */
 const char *tgemm_mfma_variant_name(int variant);
 
@@ -98,6 +132,12 @@ int tgemm_sgemm_variant_for(int64_t M, int64_t N, int64_t K,
                             const float *A, int64_t lda,
                             const float *B, int64_t ldb,
                             const float *C, int64_t ldc);
+
+/* The variant tgemm_sgemm_ex would run for these arguments; -1 if none applies. */
+int tgemm_sgemm_variant_for_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                               const float *A, int64_t lda,
+                               const float *B, int64_t ldb,
+                               const float *C, int64_t ldc);
 
 /*
  * Ablation 1 — one thread per output (page 1, section [Matrix

@@ -108,6 +108,53 @@ def test_argument_checks(lib, entry, args, status):
     assert ENTRY[entry](*args) == status
 
 
+N_, T_ = tg.TGEMM_OP_N, tg.TGEMM_OP_T
+
+
+@pytest.mark.parametrize("ops,args,status", [
+    ((T_, N_), (8, 4, 4, A_, 7, B_, 4, C_, 4), INVALID),    # op(A)=Aᵀ: lda >= M
+    ((T_, N_), (8, 4, 4, A_, 8, B_, 4, C_, 4), None),       # fine (no launch: see below)
+    ((N_, T_), (4, 8, 6, A_, 6, B_, 5, C_, 8), INVALID),    # op(B)=Bᵀ: ldb >= K
+    ((N_, T_), (4, 8, 6, A_, 5, B_, 6, C_, 8), INVALID),    # lda >= K still applies to A as stored
+    ((2, N_), (4, 4, 4, A_, 4, B_, 4, C_, 4), UNSUPPORTED),  # unknown op
+    ((N_, -1), (4, 4, 4, A_, 4, B_, 4, C_, 4), UNSUPPORTED),
+    ((T_, T_), (4, 4, 4, A_, 4, B_, 4, A_ + 48, 4), INVALID),  # C overlaps Aᵀ's storage (4×4)
+    ((T_, N_), (0, 4, 4, A_, 1, B_, 4, C_, 4), tg.TGEMM_SUCCESS),  # M = 0
+])
+def test_transposed_argument_checks(lib, ops, args, status):
+    if status is None:
+        # valid arguments: only ask which configuration would run (no launch)
+        M, N, K, a, lda, b, ldb, c, ldc = args
+        assert tg.tgemm_sgemm_variant_for_ex(*ops, M, N, K, 1 << 40, lda, 1 << 44, ldb, 1 << 46, ldc) >= 0
+        return
+    assert tg.tgemm_sgemm_ex(*ops, *args, None) == status
+    assert tg.tgemm_sgemm_mfma_ex(*ops, *args, 0, None) == status
+
+
+def test_transposed_variant_choice(lib):
+    names = tg.variant_names()
+
+    def chosen(op_a, op_b, M, N, K, lda, ldb):
+        v = tg.tgemm_sgemm_variant_for_ex(op_a, op_b, M, N, K, 1 << 40, lda, 1 << 44, ldb, 1 << 46, N)
+        return names[v] if v >= 0 else None
+
+    assert chosen(T_, N_, 4096, 4096, 4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
+    assert chosen(N_, T_, 8192, 8192, 8192, 8192, 8192) == "m256n128k16_w2x2_vec4"
+    assert chosen(T_, T_, 512, 512, 512, 512, 512) == "m32n32k8_s4d4_vec4"
+    # Aᵀ with M not a multiple of 4: its stored rows cannot take 16-byte loads
+    assert chosen(T_, N_, 4098, 4096, 4096, 4098, 4096).endswith("vec1")
+    # row-major A with K not a multiple of 4, but Aᵀ rows (length M) can
+    assert chosen(T_, N_, 4096, 4096, 4095, 4096, 4096).endswith("vec4")
+    # no configuration takes a transposed operand with an enormous leading dimension
+    assert chosen(T_, N_, 64, 64, 64, 1 << 28, 64) is None
+    assert tg.tgemm_sgemm_ex(T_, N_, 64, 64, 64, 1 << 40, 1 << 28, 1 << 44, 64, 1 << 46, 64, None) == UNSUPPORTED
+    # the 64-bit-pointer fallback takes operands as stored only
+    flat = [i for i, n in enumerate(names) if n.endswith("_flat")]
+    for v in flat:
+        assert tg.tgemm_sgemm_mfma_ex(T_, N_, 64, 64, 64, 1 << 40, 64, 1 << 44, 64, 1 << 46, 64, v,
+                                      None) == UNSUPPORTED
+
+
 def test_kernel_choice_checks(lib):
     args = (64, 64, 64, A_, 64, B_, 64, C_, 64)
     n = tg.tgemm_mfma_variant_count()

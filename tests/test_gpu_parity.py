@@ -100,9 +100,14 @@ def vec4_shape(M, N, K):
     return K % 4 == 0 and N % 4 == 0
 
 
-def runnable(name, M, N, K):
-    """Whether variant `name` takes contiguous aligned M×K·K×N operands."""
-    return not name.endswith("vec4") and not name.endswith("vec4_flat") or vec4_shape(M, N, K)
+def runnable(name, M, N, K, ta=False, tb=False):
+    """Whether variant `name` takes contiguous aligned operands of these
+    shapes and orders (ta: A stored K×M, tb: B stored N×K)."""
+    if (ta or tb) and name.endswith("_flat"):
+        return False
+    if "vec4" not in name:
+        return True
+    return (M if ta else K) % 4 == 0 and (K if tb else N) % 4 == 0
 
 
 def auto_variant(M, N, K):
@@ -305,6 +310,76 @@ def test_leading_dimension_beyond_buffer_offsets():
     del big
 
 
+OPS = [(True, False), (False, True), (True, True)]
+
+
+def stored(X, trans):
+    """Device tensor with logical value X, stored as is or transposed."""
+    if trans:
+        return dev(np.ascontiguousarray(X.T)).t()
+    return dev(X)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (7, 5, 3), (33, 65, 17), (64, 64, 64), (129, 100, 36),
+                                   (260, 131, 200), (300, 268, 513), (512, 512, 40)])
+def test_transposed_operands_integer_exact(M, N, K):
+    A, B = int_inputs(M, N, K, 31 * M + 7 * N + K)
+    Pi = oracle.gemm_i64(A, B)
+    for ta, tb in OPS:
+        dA, dB = stored(A, ta), stored(B, tb)
+        log(f"transposed {M}x{N}x{K} ta={ta} tb={tb}")
+        C = tg.sgemm(dA, dB)
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), Pi, f"auto ta={ta} tb={tb}")
+        for v, name in enumerate(variants()):
+            if not runnable(name, M, N, K, ta, tb):
+                continue
+            C = tg.sgemm(dA, dB, kernel="mfma", variant=v)
+            torch.cuda.synchronize()
+            assert_exact(C.cpu().numpy(), Pi, f"{name} ta={ta} tb={tb}")
+
+
+def test_transposed_operands_real_bound_and_guard_bands():
+    """Real inputs within the bound; transposed storage inside NaN-filled,
+    wider buffers, C inside sentinels."""
+    M, N, K = 1000, 1300, 700
+    A, B, _ = wl.random_matrices(M, N, K, "uniform", 17)
+    P, S = oracle.gemm(A, B)
+    for ta, tb in OPS:
+        log(f"transposed real ta={ta} tb={tb}")
+        sa = A.T if ta else A
+        sb = B.T if tb else B
+        _, va = guarded(np.ascontiguousarray(sa), 3, 8, float("nan"))
+        _, vb = guarded(np.ascontiguousarray(sb), 5, 4, float("nan"))
+        Cbig, Cv = guarded(np.zeros((M, N), np.float32), 2, 4, 12345.0)
+        tg.sgemm(va.t() if ta else va, vb.t() if tb else vb, out=Cv)
+        torch.cuda.synchronize()
+        big = Cbig.cpu().numpy()
+        assert_within_bound(big[:M, :N], P, S, K, f"ta={ta} tb={tb}")
+        outside = np.ones(big.shape, bool)
+        outside[:M, :N] = False
+        assert np.all(big[outside] == 12345.0)
+
+
+def test_transposed_identities_bit_exact():
+    """Aᵀ-stored identity times Bᵀ-stored B, and Aᵀ-stored A times a
+    Bᵀ-stored identity, are exact on real inputs for every configuration
+    that takes transposed operands."""
+    K, N, M = 136, 72, 100
+    B = wl.random_matrices(K, 1, N, "normal", 5)[0]   # K×N
+    A = wl.random_matrices(M, 1, K, "normal", 6)[0]   # M×K
+    I_k = np.eye(K, dtype=np.float32)
+    for v, name in enumerate(variants()):
+        if runnable(name, K, N, K, True, True):
+            C = tg.sgemm(stored(I_k, True), stored(B, True), kernel="mfma", variant=v)
+            torch.cuda.synchronize()
+            assert np.array_equal(C.cpu().numpy(), B), name
+        if runnable(name, M, K, K, True, True):
+            C = tg.sgemm(stored(A, True), stored(I_k, True), kernel="mfma", variant=v)
+            torch.cuda.synchronize()
+            assert np.array_equal(C.cpu().numpy(), A), name
+
+
 # ------------------------------------------------------------ identities and invariants
 
 def test_identities_bit_exact_real_inputs():
@@ -377,6 +452,45 @@ def test_worked_example_tile2():
     assert np.array_equal(run(Mx, Nx, "naive"), want)
     for v, name in enumerate(variants()):
         assert np.array_equal(run(Mx, Nx, "mfma", variant=v), want), name
+
+
+def test_graph_capture_replays():
+    """Calls captured into a HIP graph (torch.cuda.graph) replay correctly, many
+    times, with eager work and synchronisations between the replays; K = 0
+    (the fill kernel) is captured too."""
+    shapes = [(300, 260, 180), (512, 512, 512), (1030, 900, 700)]
+    ins = []
+    for s_, (M, N, K) in enumerate(shapes):
+        A, B = int_inputs(M, N, K, 70 + s_)
+        ins.append((dev(A), dev(B), torch.empty((M, N), device="cuda"), oracle.gemm_i64(A, B)))
+    Cz = torch.full((7, 9), float("nan"), device="cuda")
+    Az, Bz = torch.empty((7, 0), device="cuda"), torch.empty((0, 9), device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up outside the capture
+        for dA, dB, dC, _ in ins:
+            tg.sgemm(dA, dB, out=dC)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for dA, dB, dC, _ in ins:
+            tg.sgemm(dA, dB, out=dC)
+        tg.sgemm(Az, Bz, out=Cz)
+    for rep in range(5):
+        for _, _, dC, _ in ins:
+            dC.fill_(float("nan"))
+        Cz.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, _, dC, Pi) in ins:
+            assert_exact(dC.cpu().numpy(), Pi, f"replay {rep}")
+        cz = Cz.cpu().numpy()
+        assert np.all(cz == 0) and not np.any(np.signbit(cz)), f"replay {rep}: K = 0 fill"
+        # eager work between replays
+        x = torch.randn(1024, 1024, device="cuda")
+        _ = (x @ x).sum().item()
 
 
 # ------------------------------------------------------------ ABI on the device

@@ -13,6 +13,8 @@ tiled_gemm_tgemm_amd.build``).
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
+    TGEMM_OP_N,
+    TGEMM_OP_T,
     TGEMM_ERROR_HIP,
     TGEMM_ERROR_INVALID_VALUE,
     TGEMM_ERROR_NOT_SUPPORTED,
@@ -22,8 +24,11 @@ from ._lib import (  # noqa: F401
     tgemm_mfma_variant_count,
     tgemm_mfma_variant_name,
     tgemm_sgemm,
+    tgemm_sgemm_ex,
     tgemm_sgemm_lds,
     tgemm_sgemm_mfma,
+    tgemm_sgemm_mfma_ex,
+    tgemm_sgemm_variant_for_ex,
     tgemm_sgemm_naive,
     tgemm_sgemm_variant_for,
     tgemm_status_string,
@@ -33,52 +38,67 @@ from ._lib import (  # noqa: F401
 KERNELS = ("auto", "mfma", "naive", "lds")
 
 
-def _operand(t, name):
+def _check(t, name):
     import torch
 
     if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
         raise TypeError(f"{name} must be a 2-D float32 torch tensor")
     if not t.is_cuda:
         raise TypeError(f"{name} must live on a GPU")
-    if t.stride(1) != 1 and t.size(1) > 1:
-        raise ValueError(f"{name} must be row-major (unit stride along columns)")
     return t
 
 
-def _ld(t):
-    return max(t.stride(0), t.size(1), 1)
+def _layout(t, name):
+    """(op, ld) of a 2-D tensor: row-major (TGEMM_OP_N, row stride) or a
+    transposed view of a row-major matrix (TGEMM_OP_T, column stride)."""
+    rows, cols = t.shape
+    if t.stride(1) == 1 or cols <= 1:
+        return TGEMM_OP_N, max(t.stride(0), cols, 1)
+    if t.stride(0) == 1 or rows <= 1:
+        return TGEMM_OP_T, max(t.stride(1), rows, 1)
+    raise ValueError(f"{name} must be row-major or a transposed row-major view")
 
 
 def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream=None):
-    """C = A·B for float32 CUDA tensors (row-major, any leading dimension).
+    """C = A·B for float32 CUDA tensors.
 
-    kernel: "auto" (tgemm_sgemm), "mfma" (tgemm_sgemm_mfma with `variant`;
-    without one it is "auto"),
-    "naive" (tgemm_sgemm_naive) or "lds" (tgemm_sgemm_lds with tile/pad).
-    The call is queued on `stream` (default: torch's current stream) and
-    returns `out` without waiting.
+    A and B may be row-major with any leading dimension, or transposed views
+    of row-major matrices (e.g. X.t()); those are passed as TGEMM_OP_T, with
+    no copy.  `out` must be row-major.
+    kernel: "auto" (tgemm_sgemm_ex), "mfma" (tgemm_sgemm_mfma_ex with
+    `variant`; without one it is "auto"), "naive" (tgemm_sgemm_naive) or
+    "lds" (tgemm_sgemm_lds with tile/pad) — the last two for row-major
+    operands only.  The call is queued on `stream` (default: torch's current
+    stream) and returns `out` without waiting.
     """
     import torch
 
-    A = _operand(A, "A")
-    B = _operand(B, "B")
+    A = _check(A, "A")
+    B = _check(B, "B")
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    op_a, lda = _layout(A, "A")
+    op_b, ldb = _layout(B, "B")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     else:
-        out = _operand(out, "out")
+        out = _check(out, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must be {M}x{N}")
+        if out.stride(1) != 1 and N > 1:
+            raise ValueError("out must be row-major")
+    ldc = max(out.stride(0), N, 1)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
-    args = (M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), out.data_ptr(), _ld(out))
+    args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc)
+    if kernel in ("naive", "lds") and (op_a, op_b) != (TGEMM_OP_N, TGEMM_OP_N):
+        raise ValueError(f"the {kernel} kernel takes row-major operands only")
     if kernel == "auto" or (kernel == "mfma" and variant is None):
-        st = tgemm_sgemm(*args, stream)
+        st = tgemm_sgemm_ex(op_a, op_b, *args, stream)
     elif kernel == "mfma":
-        st = tgemm_sgemm_mfma(*args, variant, stream)
+        st = tgemm_sgemm_mfma_ex(op_a, op_b, *args, variant, stream)
     elif kernel == "naive":
         st = tgemm_sgemm_naive(*args, stream)
     elif kernel == "lds":

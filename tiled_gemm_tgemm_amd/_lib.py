@@ -23,8 +23,14 @@ TGEMM_ERROR_HIP = 3
 _i64 = ctypes.c_int64
 _ptr = ctypes.c_void_p
 _GEMM = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64]
+TGEMM_OP_N = 0
+TGEMM_OP_T = 1
+
 SIGNATURES = {
     "tgemm_sgemm": (ctypes.c_int, _GEMM + [_ptr]),
+    "tgemm_sgemm_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + _GEMM + [_ptr]),
+    "tgemm_sgemm_mfma_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + _GEMM + [ctypes.c_int, _ptr]),
+    "tgemm_sgemm_variant_for_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + _GEMM),
     "tgemm_sgemm_mfma": (ctypes.c_int, _GEMM + [ctypes.c_int, _ptr]),
     "tgemm_mfma_variant_count": (ctypes.c_int, []),
     "tgemm_mfma_variant_name": (ctypes.c_char_p, [ctypes.c_int]),
@@ -64,6 +70,18 @@ def library():
 
 def tgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return library().tgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return library().tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tgemm_sgemm_mfma_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, variant, stream=None) -> int:
+    return library().tgemm_sgemm_mfma_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, variant, stream)
+
+
+def tgemm_sgemm_variant_for_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return library().tgemm_sgemm_variant_for_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc)
 
 
 def tgemm_sgemm_mfma(M, N, K, A, lda, B, ldb, C, ldc, variant, stream=None) -> int:

@@ -31,13 +31,13 @@ enum class Quick { kNone, kDone, kZeroFill };
 
 // Shared checks of every compute entry point.  On success `quick` says
 // whether the call is already complete (M or N zero) or only needs C zeroed
-// (K zero).
-tgemm_status_t validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+// (K zero).  ta / tb: A stored K×M, B stored N×K.
+tgemm_status_t validate(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                         const float *B, int64_t ldb, const float *C, int64_t ldc, Quick &quick)
 {
     quick = Quick::kNone;
     if (M < 0 || N < 0 || K < 0) return TGEMM_ERROR_INVALID_VALUE;
-    if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return TGEMM_ERROR_INVALID_VALUE;
+    if (lda < max1(ta ? M : K) || ldb < max1(tb ? K : N) || ldc < max1(N)) return TGEMM_ERROR_INVALID_VALUE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TGEMM_ERROR_NOT_SUPPORTED;
     if (lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40 || ldc > (int64_t)1 << 40)
         return TGEMM_ERROR_NOT_SUPPORTED;
@@ -54,37 +54,41 @@ tgemm_status_t validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t
     if (reinterpret_cast<uintptr_t>(A) % alignof(float) || reinterpret_cast<uintptr_t>(B) % alignof(float))
         return TGEMM_ERROR_INVALID_VALUE;
     uintptr_t a0, a1, b0, b1, c0, c1;
-    span(A, M, K, lda, a0, a1);
-    span(B, K, N, ldb, b0, b1);
+    span(A, ta ? K : M, ta ? M : K, lda, a0, a1);
+    span(B, tb ? N : K, tb ? K : N, ldb, b0, b1);
     span(C, M, N, ldc, c0, c1);
     if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return TGEMM_ERROR_INVALID_VALUE;
     return TGEMM_SUCCESS;
 }
 
-GemmArgs pack(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
-              int64_t ldb, float *C, int64_t ldc)
+GemmArgs pack(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+              const float *B, int64_t ldb, float *C, int64_t ldc)
 {
-    return GemmArgs{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc};
+    return GemmArgs{(int)M, (int)N, (int)K, A, lda, B, ldb, C, ldc, ta, tb};
 }
 
 tgemm_status_t from_hip(hipError_t e) { return e == hipSuccess ? TGEMM_SUCCESS : TGEMM_ERROR_HIP; }
 
 bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
-// 16-byte loads need every row start 16-byte aligned and whole float4s
-// inside the logical row (K and N multiples of 4).
-bool vec4_ok(int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
-             const float *C, int64_t ldc)
+// 16-byte loads need every stored row of A and B to start 16-byte aligned and
+// to hold whole float4s: the stored row lengths (K or M for A, N or K for B)
+// and the leading dimensions must be multiples of 4.
+bool vec4_ok(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+             const float *B, int64_t ldb)
 {
-    return aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
-           ldc % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+    return aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0 && (ta ? M : K) % 4 == 0 &&
+           (tb ? K : N) % 4 == 0;
 }
 
 // Whether a configuration can run these operands: 16-byte loads need
-// vec4_ok, and buffer-load configurations bound the leading dimensions.
-bool runs(const tgemm::MfmaVariant &v, bool vec4, int64_t lda, int64_t ldb)
+// vec4_ok, buffer-load configurations bound the leading dimensions, and the
+// 64-bit-pointer fallback takes operands as stored only.
+bool runs(const tgemm::MfmaVariant &v, bool vec4, bool ta, bool tb, int64_t lda, int64_t ldb)
 {
-    return (v.vec == 1 || vec4) && lda <= v.max_lda && ldb <= v.max_ldb;
+    if ((ta || tb) && !v.trans) return false;
+    return (v.vec == 1 || vec4) && lda <= (ta ? v.max_lda_t : v.max_lda) &&
+           ldb <= (tb ? v.max_ldb_t : v.max_ldb);
 }
 
 // Estimated time of a configuration in SIMD cycles.  Work-groups are dealt
@@ -115,15 +119,15 @@ double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
     return t;
 }
 
-int choose_variant(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
-                   int64_t ldb, const float *C, int64_t ldc)
+int choose_variant(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                   const float *B, int64_t ldb)
 {
-    const bool vec4 = vec4_ok(N, K, A, lda, B, ldb, C, ldc);
+    const bool vec4 = vec4_ok(ta, tb, M, N, K, A, lda, B, ldb);
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
-        if (!runs(*v, vec4, lda, ldb)) continue;
+        if (!runs(*v, vec4, ta, tb, lda, ldb)) continue;
         const double c = cost(*v, M, N, K);
         if (best < 0 || c < best_cost) {
             best = i;
@@ -133,34 +137,53 @@ int choose_variant(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
     return best;
 }
 
+bool op_ok(tgemm_op_t op) { return op == TGEMM_OP_N || op == TGEMM_OP_T; }
+
 }  // namespace
 
 extern "C" {
+
+tgemm_status_t tgemm_sgemm_mfma_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                                   const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                                   int64_t ldc, int variant, hipStream_t stream)
+{
+    const tgemm::MfmaVariant *v = tgemm::mfma_variant(variant);
+    if (v == nullptr || !op_ok(op_a) || !op_ok(op_b)) return TGEMM_ERROR_NOT_SUPPORTED;
+    const bool ta = op_a == TGEMM_OP_T, tb = op_b == TGEMM_OP_T;
+    Quick quick;
+    const tgemm_status_t st = validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if (!runs(*v, vec4_ok(ta, tb, M, N, K, A, lda, B, ldb), ta, tb, lda, ldb)) return TGEMM_ERROR_NOT_SUPPORTED;
+    return from_hip(v->launch(pack(ta, tb, M, N, K, A, lda, B, ldb, C, ldc), stream));
+}
 
 tgemm_status_t tgemm_sgemm_mfma(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                                 const float *B, int64_t ldb, float *C, int64_t ldc, int variant,
                                 hipStream_t stream)
 {
-    const tgemm::MfmaVariant *v = tgemm::mfma_variant(variant);
-    if (v == nullptr) return TGEMM_ERROR_NOT_SUPPORTED;
+    return tgemm_sgemm_mfma_ex(TGEMM_OP_N, TGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, variant, stream);
+}
+
+tgemm_status_t tgemm_sgemm_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                              const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                              int64_t ldc, hipStream_t stream)
+{
+    if (!op_ok(op_a) || !op_ok(op_b)) return TGEMM_ERROR_NOT_SUPPORTED;
+    const bool ta = op_a == TGEMM_OP_T, tb = op_b == TGEMM_OP_T;
     Quick quick;
-    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    const tgemm_status_t st = validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick);
     if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
-    if (!runs(*v, vec4_ok(N, K, A, lda, B, ldb, C, ldc), lda, ldb)) return TGEMM_ERROR_NOT_SUPPORTED;
-    return from_hip(v->launch(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
+    const int variant = choose_variant(ta, tb, M, N, K, A, lda, B, ldb);
+    if (variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
+    return from_hip(tgemm::mfma_variant(variant)->launch(pack(ta, tb, M, N, K, A, lda, B, ldb, C, ldc), stream));
 }
 
 tgemm_status_t tgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                            const float *B, int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
 {
-    Quick quick;
-    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
-    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
-    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
-    const int variant = choose_variant(M, N, K, A, lda, B, ldb, C, ldc);
-    if (variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
-    return from_hip(tgemm::mfma_variant(variant)->launch(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
+    return tgemm_sgemm_ex(TGEMM_OP_N, TGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int tgemm_mfma_variant_count(void) { return tgemm::mfma_variant_count(); }
@@ -171,13 +194,22 @@ const char *tgemm_mfma_variant_name(int variant)
     return v ? v->name : nullptr;
 }
 
+int tgemm_sgemm_variant_for_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                               const float *A, int64_t lda, const float *B, int64_t ldb, const float *C,
+                               int64_t ldc)
+{
+    if (!op_ok(op_a) || !op_ok(op_b)) return -1;
+    const bool ta = op_a == TGEMM_OP_T, tb = op_b == TGEMM_OP_T;
+    Quick quick;
+    if (validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick) != TGEMM_SUCCESS || quick != Quick::kNone)
+        return -1;
+    return choose_variant(ta, tb, M, N, K, A, lda, B, ldb);
+}
+
 int tgemm_sgemm_variant_for(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                             const float *B, int64_t ldb, const float *C, int64_t ldc)
 {
-    Quick quick;
-    if (validate(M, N, K, A, lda, B, ldb, C, ldc, quick) != TGEMM_SUCCESS || quick != Quick::kNone)
-        return -1;
-    return choose_variant(M, N, K, A, lda, B, ldb, C, ldc);
+    return tgemm_sgemm_variant_for_ex(TGEMM_OP_N, TGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 tgemm_status_t tgemm_sgemm_naive(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
@@ -185,11 +217,11 @@ tgemm_status_t tgemm_sgemm_naive(int64_t M, int64_t N, int64_t K, const float *A
                                  hipStream_t stream)
 {
     Quick quick;
-    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    const tgemm_status_t st = validate(false, false, M, N, K, A, lda, B, ldb, C, ldc, quick);
     if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
     if ((M + 15) / 16 > 65535) return TGEMM_ERROR_NOT_SUPPORTED;  // grid rows limit
-    return from_hip(tgemm::launch_naive(pack(M, N, K, A, lda, B, ldb, C, ldc), stream));
+    return from_hip(tgemm::launch_naive(pack(false, false, M, N, K, A, lda, B, ldb, C, ldc), stream));
 }
 
 tgemm_status_t tgemm_sgemm_lds(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
@@ -199,11 +231,11 @@ tgemm_status_t tgemm_sgemm_lds(int64_t M, int64_t N, int64_t K, const float *A, 
     if (!(tile == 2 || tile == 8 || tile == 16 || tile == 32) || !(pad == 0 || pad == 1))
         return TGEMM_ERROR_NOT_SUPPORTED;
     Quick quick;
-    const tgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, quick);
+    const tgemm_status_t st = validate(false, false, M, N, K, A, lda, B, ldb, C, ldc, quick);
     if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
     if ((M + tile - 1) / tile > 65535) return TGEMM_ERROR_NOT_SUPPORTED;  // grid rows limit
-    return from_hip(tgemm::launch_lds_tiled(pack(M, N, K, A, lda, B, ldb, C, ldc), tile, pad, stream));
+    return from_hip(tgemm::launch_lds_tiled(pack(false, false, M, N, K, A, lda, B, ldb, C, ldc), tile, pad, stream));
 }
 
 const char *tgemm_status_string(tgemm_status_t status)

@@ -38,28 +38,39 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int group_m, i
     tn = in_group / rows;
 }
 
-// One wavefront's view of a phase held in LDS: As holds the BM×BK slice of A
-// (row-major, layout chosen by the kernel), Bs[k][n] the BK×BN slice of B
-// with row stride BS words.  In step s of k-group g the lanes of half h feed
-// k = 8g + 4h + s to both operands, so a lane's four A values of a group are
-// adjacent and come in one 16-byte read.
-template <int FM, int FN, int BS>
+// Reading one operand's fragments for a k-group from an LDS stage.  In step
+// s of k-group g the lanes of half h feed k = 8g + 4h + s to both operands,
+// so each lane needs four consecutive values of k per 32-row (or 32-column)
+// block.  A slice kept k-contiguous ([mn][k], KC) gives them in one 16-byte
+// read at `off`; a slice kept mn-contiguous ([k][mn], row stride S words)
+// gives them in four 4-byte reads at off, off + S, off + 2S, off + 3S.
+template <bool KC, int S>
+__device__ __forceinline__ f32x4 read_frag(const float *base, int off)
+{
+    if constexpr (KC) {
+        return *reinterpret_cast<const f32x4 *>(base + off);
+    } else {
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = base[off + q * S];
+        return v;
+    }
+}
+
+// One wavefront's fragments of one k-group: a[i] for its FM row blocks of A,
+// b[j] for its FN column blocks of B.
+template <int FM, int FN, bool A_KC, int AS, bool B_KC, int BS>
 struct Fragments {
     f32x4 a[FM];
-    float b[FN][4];
+    f32x4 b[FN];
 
-    // a_off[i]: word offset in As of (row wm*TM + 32i + l32, columns 8g+4h ..
-    // 8g+4h+3) for this group g; b_frag: offset of (row 4h, column
-    // wn*TN + l32) in Bs.
     __device__ __forceinline__ void read(const float *as, const float *bs, const int (&a_off)[FM],
-                                         int b_frag, int g)
+                                         const int (&b_off)[FN])
     {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const f32x4 *>(as + a_off[i]);
+        for (int i = 0; i < FM; ++i) a[i] = read_frag<A_KC, AS>(as, a_off[i]);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) b[j][s] = bs[b_frag + (8 * g + s) * BS + j * 32];
+        for (int j = 0; j < FN; ++j) b[j] = read_frag<B_KC, BS>(bs, b_off[j]);
     }
 };
 
@@ -76,17 +87,27 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[FM][FN], const Frag &f)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[j][s], acc[i][j], 0, 0, 0);
 }
 
-// A whole phase of BK values of k from one LDS stage; the reads of group
-// g+1 are issued before the matrix-core steps of group g.
-template <int FM, int FN, int BS, int BK>
-__device__ __forceinline__ void mfma_phase(f32x16 (&acc)[FM][FN], const float *as, const float *bs,
-                                           const int (&a_off)[BK / 8][FM], int b_frag)
+// Word offset of this lane's fragment of block `blk` (32 rows of A or 32
+// columns of B, counted from the wavefront's first) for k-group g, in a
+// slice kept KC ([mn][k], row stride S) or MC ([k][mn], row stride S).
+template <bool KC, int S>
+__device__ __forceinline__ int frag_offset(int mn, int g, int half)
 {
-    Fragments<FM, FN, BS> f[2];
-    f[0].read(as, bs, a_off[0], b_frag, 0);
+    return KC ? mn * S + 8 * g + 4 * half : (8 * g + 4 * half) * S + mn;
+}
+
+// A whole phase of BK values of k from one LDS stage; the reads of group
+// g+1 are issued before the matrix-core steps of group g.  a_off[g][i] and
+// b_off[g][j] come from frag_offset.
+template <int FM, int FN, int BK, bool A_KC, int AS, bool B_KC, int BS>
+__device__ __forceinline__ void mfma_phase(f32x16 (&acc)[FM][FN], const float *as, const float *bs,
+                                           const int (&a_off)[BK / 8][FM], const int (&b_off)[BK / 8][FN])
+{
+    Fragments<FM, FN, A_KC, AS, B_KC, BS> f[2];
+    f[0].read(as, bs, a_off[0], b_off[0]);
 #pragma unroll
     for (int g = 0; g < BK / 8; ++g) {
-        if (g + 1 < BK / 8) f[(g + 1) & 1].read(as, bs, a_off[g + 1], b_frag, g + 1);
+        if (g + 1 < BK / 8) f[(g + 1) & 1].read(as, bs, a_off[g + 1], b_off[g + 1]);
         mfma_group<FM, FN>(acc, f[g & 1]);
     }
 }

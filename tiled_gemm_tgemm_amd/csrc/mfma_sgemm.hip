@@ -45,6 +45,13 @@
 //   mfma_common.h.  The summation order is not part of the product's
 //   definition; rounding stays within the accepted bound and integer inputs
 //   whose partial sums stay below 2^24 come out exact.
+// * Transposed operands: an operand is read from device memory along the
+//   dimension it is contiguous in and kept in LDS the same way — k-contiguous
+//   slices as [mn][k] (A as stored, or B transposed), mn-contiguous ones as
+//   [k][mn] (B as stored, or A transposed) — and mfma_common.h reads either
+//   layout.  No operand is transposed on the way (page 1, section
+//   [Coalescing], "Corner Turning": load in the coalesced order, read on chip
+//   in the order the arithmetic needs).
 #include "mfma_common.h"
 #include "tgemm_kernels.h"
 
@@ -56,31 +63,6 @@ using mfma::f32x4;
 using mfma::kWave;
 
 constexpr uint32_t kOutside = 0x80000000u;  // an offset beyond every extent (all are < 2^31)
-
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int VEC_, int GROUP_M_, int OCC_>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, VEC = VEC_;
-    static constexpr int GROUP_M = GROUP_M_;
-    static constexpr int OCC = OCC_;                   // wavefronts per SIMD to budget registers for
-    static constexpr int NT = kWave * WM * WN;         // threads per work-group
-    static constexpr int TM = BM / WM, TN = BN / WN;   // wavefront sub-tile
-    static constexpr int FM = TM / 32, FN = TN / 32;   // 32×32 blocks per wavefront
-    static constexpr int AS = BK + 4;                  // As row stride (words)
-    static constexpr int BS = BN + 8;                  // Bs row stride (words)
-    static constexpr int A_STAGE = BM * AS;
-    static constexpr int STAGE = A_STAGE + BK * BS;
-    static constexpr int LDS_WORDS = 2 * STAGE;
-    static constexpr int LA = BM * BK / (VEC * NT);    // A loads per thread per phase
-    static constexpr int LB = BK * BN / (VEC * NT);    // B loads per thread per phase
-    static constexpr int RA = NT * VEC / BK;           // rows between a thread's A slots
-    static constexpr int RB = NT * VEC / BN;           // rows between a thread's B slots
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront sub-tile must be 32-aligned");
-    static_assert(BK % 8 == 0, "phase depth must be a multiple of 8");
-    static_assert((NT * VEC) % BK == 0 && (NT * VEC) % BN == 0 && LA >= 1 && LB >= 1 &&
-                      LA * RA == BM && LB * RB == BK,
-                  "slices must split into whole rows per load step");
-    static_assert(LDS_WORDS * 4 <= 160 * 1024, "LDS budget of one gfx950 CU");
-};
 
 template <int VEC>
 struct Vec;
@@ -101,13 +83,97 @@ struct Vec<1> {
     }
 };
 
-// Raw buffer over [base, base + bytes); bytes is clamped to 2^31 - 1, which
-// only ever shortens an extent that reaches beyond every offset in use.
+// Raw buffer over [base, base + bytes); bytes is clamped to [0, 2^31 - 1],
+// which only ever shortens an extent that reaches beyond every offset in use.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const float *base, int64_t bytes)
 {
-    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n, 0x00020000);
 }
+
+// One operand's per-phase copy: a MN×BK slice (MN = BM for A, BN for B) read
+// from device memory and written to one LDS stage.
+//   KC: the operand is k-contiguous in memory (A as stored, B transposed):
+//       element (mn, k) at ptr[mn*ld + k]; LDS keeps [mn][k], row stride BK+4.
+//   MC: mn-contiguous (B as stored, A transposed): element (mn, k) at
+//       ptr[k*ld + mn]; LDS keeps [k][mn], row stride MN+8.
+// Each thread owns L slots of VEC consecutive elements along the contiguous
+// dimension; consecutive threads own consecutive slots of a row.
+template <bool KC_, int MN, int BK, int VEC, int NT>
+struct Loader {
+    static constexpr bool KC = KC_;
+    static constexpr int ROWS = KC ? MN : BK;           // rows of the slice as stored
+    static constexpr int COLS = KC ? BK : MN;           // contiguous extent of a row
+    static constexpr int S = KC ? BK + 4 : MN + 8;      // LDS row stride (words)
+    static constexpr int WORDS = ROWS * S;              // one LDS stage
+    static constexpr int L = ROWS * COLS / (VEC * NT);  // slots per thread
+    static constexpr int R = NT * VEC / COLS;           // rows between a thread's slots
+    static_assert((NT * VEC) % COLS == 0 && L >= 1 && L * R == ROWS, "slice splits into whole rows");
+
+    typedef typename Vec<VEC>::type vec_t;
+    uint32_t off[L];  // byte offset of each slot from the slice's first element
+    int c;            // contiguous coordinate of the thread's slots
+    int st;           // LDS word offset of slot 0 (slot i adds i*R*S)
+    vec_t reg[L];
+
+    // mn_valid: rows (KC) or columns (MC) of this tile inside the matrix.
+    __device__ __forceinline__ void init(int t, int64_t ld, int mn_valid)
+    {
+        const int r0 = t * VEC / COLS;
+        c = t * VEC % COLS;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int r = r0 + i * R;
+            const bool in = KC ? r < mn_valid : c < mn_valid;
+            off[i] = in ? (uint32_t)((r * ld + c) * 4) : kOutside;
+        }
+        st = r0 * S + c;
+    }
+
+    // Issue the loads of the phase starting at k0.  tile = operand pointer at
+    // (mn0, 0); K_end: end of the summed range.  Reads past the extent give
+    // zero; for KC operands the columns k >= K_end of a partial phase are cut
+    // explicitly (for MC they lie past the extent).
+    __device__ __forceinline__ void issue(const float *tile, int64_t ld, int k0, int K_end, int mn_valid,
+                                          bool partial)
+    {
+        const __amdgpu_buffer_rsrc_t rs =
+            KC ? buffer(tile + k0, ((int64_t)(mn_valid - 1) * ld + (K_end - k0)) * 4)
+               : buffer(tile + (int64_t)k0 * ld, ((int64_t)(K_end - k0 - 1) * ld + mn_valid) * 4);
+        const bool cut = KC && partial && k0 + c >= K_end;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const uint32_t o = cut ? kOutside : off[i];
+            reg[i] = Vec<VEC>::load(rs, o);
+        }
+    }
+
+    __device__ __forceinline__ void store(float *stage) const
+    {
+#pragma unroll
+        for (int i = 0; i < L; ++i) *reinterpret_cast<vec_t *>(stage + st + i * R * S) = reg[i];
+    }
+};
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int VEC_, int GROUP_M_, int OCC_, bool TA_,
+          bool TB_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, VEC = VEC_;
+    static constexpr int GROUP_M = GROUP_M_;
+    static constexpr int OCC = OCC_;                   // wavefronts per SIMD to budget registers for
+    static constexpr bool TA = TA_, TB = TB_;          // operands stored transposed
+    static constexpr int NT = kWave * WM * WN;         // threads per work-group
+    static constexpr int TM = BM / WM, TN = BN / WN;   // wavefront sub-tile
+    static constexpr int FM = TM / 32, FN = TN / 32;   // 32×32 blocks per wavefront
+    typedef Loader<!TA, BM, BK, VEC, NT> LA;           // A as stored is k-contiguous
+    typedef Loader<TB, BN, BK, VEC, NT> LB;            // B as stored is n-contiguous
+    static constexpr int A_STAGE = LA::WORDS;
+    static constexpr int STAGE = A_STAGE + LB::WORDS;
+    static constexpr int LDS_WORDS = 2 * STAGE;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront sub-tile must be 32-aligned");
+    static_assert(BK % 8 == 0, "phase depth must be a multiple of 8");
+    static_assert(LDS_WORDS * 4 <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
 
 template <class G>
 __global__ __launch_bounds__(G::NT) __attribute__((amdgpu_waves_per_eu(G::OCC, G::OCC)))
@@ -115,8 +181,8 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
                        const float *__restrict__ B, int64_t ldb, float *__restrict__ C,
                        int64_t ldc)
 {
-    typedef typename Vec<G::VEC>::type vec_t;
-    constexpr int VEC = G::VEC;
+    typedef typename G::LA LA;
+    typedef typename G::LB LB;
 
     __shared__ __attribute__((aligned(16))) float lds[G::LDS_WORDS];
 
@@ -132,58 +198,21 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
     const int wm = wave / G::WN, wn = wave % G::WN;
     const int l32 = lane % 32, half = lane / 32;
 
-    // Load slots.  A slot i: row a_r0 + i*RA, columns a_c .. a_c+VEC-1 of the
-    // BM×BK slice; B slot i: row b_r0 + i*RB, columns b_c .. b_c+VEC-1 of the
-    // BK×BN slice.  Offsets are in bytes from the slice's first element.
-    const int a_r0 = t * VEC / G::BK, a_c = t * VEC % G::BK;
-    const int b_r0 = t * VEC / G::BN, b_c = t * VEC % G::BN;
-    uint32_t a_off[G::LA], b_off[G::LB];
-#pragma unroll
-    for (int i = 0; i < G::LA; ++i) {
-        const int r = a_r0 + i * G::RA;
-        a_off[i] = r < rows_valid ? (uint32_t)((r * lda + a_c) * 4) : kOutside;
-    }
-#pragma unroll
-    for (int i = 0; i < G::LB; ++i) {
-        const int r = b_r0 + i * G::RB;
-        b_off[i] = b_c < cols_valid ? (uint32_t)((r * ldb + b_c) * 4) : kOutside;
-    }
-    const float *a_panel = A + (int64_t)m0 * lda;
-    const float *b_panel = B + n0;
-
-    vec_t a_reg[G::LA], b_reg[G::LB];
-    // Issue the loads of the phase starting at k0.  `partial` marks the last
-    // phase when K is not a multiple of BK: A columns >= K are then read as
-    // zero explicitly (B's rows >= K lie past its extent anyway).
+    LA la;
+    LB lb;
+    la.init(t, lda, rows_valid);
+    lb.init(t, ldb, cols_valid);
+    // operand pointers at (m0, 0) and (n0, 0) in their own storage order
+    const float *a_tile = A + (LA::KC ? (int64_t)m0 * lda : (int64_t)m0);
+    const float *b_tile = B + (LB::KC ? (int64_t)n0 * ldb : (int64_t)n0);
     auto load_phase = [&] __device__(int k0, bool partial) {
-        const __amdgpu_buffer_rsrc_t ra =
-            buffer(a_panel + k0, ((int64_t)(rows_valid - 1) * lda + (K - k0)) * 4);
-        const __amdgpu_buffer_rsrc_t rb =
-            buffer(b_panel + (int64_t)k0 * ldb, ((int64_t)(K - k0 - 1) * ldb + cols_valid) * 4);
-        const bool a_cut = partial && k0 + a_c >= K;
-#pragma unroll
-        for (int i = 0; i < G::LA; ++i) {
-            const uint32_t off = a_cut ? kOutside : a_off[i];
-            a_reg[i] = Vec<VEC>::load(ra, off);
-        }
-#pragma unroll
-        for (int i = 0; i < G::LB; ++i) {
-            const uint32_t off = b_off[i];
-            b_reg[i] = Vec<VEC>::load(rb, off);
-        }
+        la.issue(a_tile, lda, k0, K, rows_valid, partial);
+        lb.issue(b_tile, ldb, k0, K, cols_valid, partial);
     };
-    // LDS word offset of each A slot in a stage
-    int a_st[G::LA];
-#pragma unroll
-    for (int i = 0; i < G::LA; ++i) a_st[i] = (a_r0 + i * G::RA) * G::AS + a_c;
-    float *b_st = lds + G::A_STAGE + b_r0 * G::BS + b_c;
     auto store_phase = [&] __device__(int stage) {
-#pragma unroll
-        for (int i = 0; i < G::LA; ++i)
-            *reinterpret_cast<vec_t *>(lds + stage * G::STAGE + a_st[i]) = a_reg[i];
-#pragma unroll
-        for (int i = 0; i < G::LB; ++i)
-            *reinterpret_cast<vec_t *>(b_st + stage * G::STAGE + i * G::RB * G::BS) = b_reg[i];
+        float *s = lds + stage * G::STAGE;
+        la.store(s);
+        lb.store(s + G::A_STAGE);
     };
 
     f32x16 acc[G::FM][G::FN];
@@ -192,15 +221,20 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-    int a_frag[G::BK / 8][G::FM];
+    int a_frag[G::BK / 8][G::FM], b_frag[G::BK / 8][G::FN];
 #pragma unroll
-    for (int g = 0; g < G::BK / 8; ++g)
+    for (int g = 0; g < G::BK / 8; ++g) {
 #pragma unroll
-        for (int i = 0; i < G::FM; ++i) a_frag[g][i] = (wm * G::TM + i * 32 + l32) * G::AS + 8 * g + 4 * half;
-    const int b_frag = (4 * half) * G::BS + wn * G::TN + l32;
+        for (int i = 0; i < G::FM; ++i)
+            a_frag[g][i] = mfma::frag_offset<LA::KC, LA::S>(wm * G::TM + i * 32 + l32, g, half);
+#pragma unroll
+        for (int j = 0; j < G::FN; ++j)
+            b_frag[g][j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, g, half);
+    }
     auto compute = [&] __device__(int stage) {
-        const float *as = lds + stage * G::STAGE;
-        mfma::mfma_phase<G::FM, G::FN, G::BS, G::BK>(acc, as, as + G::A_STAGE, a_frag, b_frag);
+        const float *s = lds + stage * G::STAGE;
+        mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, s, s + G::A_STAGE,
+                                                                               a_frag, b_frag);
     };
 
     const int full = K / G::BK;            // phases with all BK values of k
@@ -241,14 +275,6 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream)
                            dim3((unsigned)tiles), dim3(G::NT), args, 0, stream);
 }
 
-//           BM   BN  BK WM WN VEC GROUP_M OCC
-typedef Cfg<256, 128, 16, 2, 2, 4, 4, 2> Large4;
-typedef Cfg<128, 128, 32, 2, 2, 4, 8, 2> Mid4;
-typedef Cfg<64, 64, 32, 2, 2, 4, 8, 4> Small4;
-typedef Cfg<256, 128, 16, 2, 2, 1, 4, 2> Large1;
-typedef Cfg<128, 128, 32, 2, 2, 1, 8, 2> Mid1;
-typedef Cfg<64, 64, 32, 2, 2, 1, 8, 4> Small1;
-
 template <class G>
 constexpr int wg_per_cu()
 {
@@ -256,23 +282,47 @@ constexpr int wg_per_cu()
 }
 
 // Buffer offsets are 32-bit and kept below 2^31: a slot's offset spans at
-// most BM rows of A or BK rows of B, which bounds the leading dimensions
-// these configurations take.
-template <class G>
-constexpr int64_t max_lda()
+// most ROWS rows of its operand as stored, which bounds the leading
+// dimensions a configuration takes.
+template <class L>
+constexpr int64_t max_ld()
 {
-    return ((((int64_t)1 << 31) - 16) / 4) / G::BM;
-}
-template <class G>
-constexpr int64_t max_ldb()
-{
-    return ((((int64_t)1 << 31) - 16) / 4 - G::BN) / G::BK;
+    return ((((int64_t)1 << 31) - 16) / 4 - L::COLS) / L::ROWS;
 }
 
-#define TGEMM_VARIANT(name, G, alone, full)                                                    \
-    {                                                                                           \
-        name, G::BM, G::BN, G::BK, G::VEC, wg_per_cu<G>(), max_lda<G>(), max_ldb<G>(), alone, \
-            full, 7000.0, &launch_cfg<G>                                                        \
+// One tile shape in its four operand orders (NN, TN, NT, TT).
+template <int BM, int BN, int BK, int VEC, int GM, int OCC>
+struct Shape {
+    template <bool TA, bool TB>
+    using C = Cfg<BM, BN, BK, 2, 2, VEC, GM, OCC, TA, TB>;
+    static hipError_t launch(const GemmArgs &g, hipStream_t stream)
+    {
+        switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
+            case 0: return launch_cfg<C<false, false>>(g, stream);
+            case 1: return launch_cfg<C<true, false>>(g, stream);
+            case 2: return launch_cfg<C<false, true>>(g, stream);
+            default: return launch_cfg<C<true, true>>(g, stream);
+        }
+    }
+};
+
+//             BM   BN  BK VEC GROUP_M OCC
+typedef Shape<256, 128, 16, 4, 4, 2> Large4;
+typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
+typedef Shape<64, 64, 32, 4, 8, 4> Small4;
+typedef Shape<256, 128, 16, 1, 4, 2> Large1;
+typedef Shape<128, 128, 32, 1, 8, 2> Mid1;
+typedef Shape<64, 64, 32, 1, 8, 4> Small1;
+
+#define TGEMM_VARIANT(name, S, alone, full)                                                         \
+    {                                                                                                \
+        name, S::template C<false, false>::BM, S::template C<false, false>::BN,                     \
+            S::template C<false, false>::BK, S::template C<false, false>::VEC,                      \
+            wg_per_cu<typename S::template C<false, false>>(),                                      \
+            max_ld<typename S::template C<false, false>::LA>(),                                     \
+            max_ld<typename S::template C<false, false>::LB>(),                                     \
+            max_ld<typename S::template C<true, false>::LA>(),                                      \
+            max_ld<typename S::template C<false, true>::LB>(), true, alone, full, 7000.0, &S::launch \
     }
 
 // Efficiencies measured on MI355X (square and ragged shapes from 512 to 8192).

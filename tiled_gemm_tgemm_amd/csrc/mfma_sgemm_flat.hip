@@ -1,5 +1,5 @@
 // Matrix-core kernel for operands whose leading dimensions are too large for
-// the 32-bit buffer offsets of mfma_sgemm.hip.  Same product, same tiling
+// the 32-bit buffer offsets of mfma_sgemm.hip (operands as stored only).  Same product, same tiling
 // plan (page 1, "[Multi-Core & GPU Programming] CUDA - Matrix
 // Multiplication", section [Shared Memory]; page 2, "Lec 29 · GPU
 // Architecture (2)", §1.2): 128×128 tiles, phases of 32 values of k, two LDS
@@ -127,12 +127,16 @@ void mfma_sgemm_flat_kernel(int M, int N, int K, const float *__restrict__ A, in
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-    int a_off[G::BK / 8][G::FM];
+    int a_frag[G::BK / 8][G::FM], b_frag[G::BK / 8][G::FN];
 #pragma unroll
-    for (int g = 0; g < G::BK / 8; ++g)
+    for (int g = 0; g < G::BK / 8; ++g) {
 #pragma unroll
-        for (int i = 0; i < G::FM; ++i) a_off[g][i] = (wm * G::TM + i * 32 + l32) * G::AS + 8 * g + 4 * half;
-    const int b_frag = (4 * half) * G::BS + wn * G::TN + l32;
+        for (int i = 0; i < G::FM; ++i)
+            a_frag[g][i] = mfma::frag_offset<true, G::AS>(wm * G::TM + i * 32 + l32, g, half);
+#pragma unroll
+        for (int j = 0; j < G::FN; ++j)
+            b_frag[g][j] = mfma::frag_offset<false, G::BS>(wn * G::TN + j * 32 + l32, g, half);
+    }
     const int phases = (K + G::BK - 1) / G::BK;
     load_phase(0);
     store_phase(0, 0);
@@ -141,7 +145,8 @@ void mfma_sgemm_flat_kernel(int M, int N, int K, const float *__restrict__ A, in
         const bool more = p + 1 < phases;
         if (more) load_phase((p + 1) * G::BK);
         const float *as = lds + (p & 1) * G::STAGE;
-        mfma::mfma_phase<G::FM, G::FN, G::BS, G::BK>(acc, as, as + G::A_STAGE, a_off, b_frag);
+        mfma::mfma_phase<G::FM, G::FN, G::BK, true, G::AS, false, G::BS>(acc, as, as + G::A_STAGE, a_frag,
+                                                                         b_frag);
         if (more) store_phase((p + 1) & 1, (p + 1) * G::BK);
         __syncthreads();
     }
@@ -167,8 +172,10 @@ typedef FlatCfg<128, 128, 32, 2, 2, 4, 8, 2> Flat4;
 typedef FlatCfg<128, 128, 32, 2, 2, 1, 8, 2> Flat1;
 
 const MfmaVariant kFlatVariants[] = {
-    {"m128n128k32_w2x2_vec4_flat", 128, 128, 32, 4, 2, INT64_MAX, INT64_MAX, 0.55, 0.75, 7000.0, &launch_flat<Flat4>},
-    {"m128n128k32_w2x2_vec1_flat", 128, 128, 32, 1, 2, INT64_MAX, INT64_MAX, 0.45, 0.60, 7000.0, &launch_flat<Flat1>},
+    {"m128n128k32_w2x2_vec4_flat", 128, 128, 32, 4, 2, INT64_MAX, INT64_MAX, 0, 0, false, 0.55, 0.75, 7000.0,
+     &launch_flat<Flat4>},
+    {"m128n128k32_w2x2_vec1_flat", 128, 128, 32, 1, 2, INT64_MAX, INT64_MAX, 0, 0, false, 0.45, 0.60, 7000.0,
+     &launch_flat<Flat1>},
 };
 
 }  // namespace

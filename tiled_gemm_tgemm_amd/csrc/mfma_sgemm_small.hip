@@ -20,6 +20,10 @@
 // * The KS partial tiles are added in LDS in a fixed order (wavefront 0 first)
 //   after one barrier — the only synchronisation — so results do not depend
 //   on timing; C is written once, 32 consecutive columns per 32 lanes.
+// * Transposed operands are read along the dimension they are contiguous in:
+//   a k-contiguous operand (A as stored, B transposed) gives a lane its four
+//   k values in one read; an mn-contiguous one (B as stored, A transposed) in
+//   four reads, each coalesced across the 32 lanes of a half-wavefront.
 #include "mfma_common.h"
 #include "tgemm_kernels.h"
 
@@ -38,9 +42,59 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t small_buffer(const float *base
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n, 0x00020000);
 }
 
-template <int KS_, int D_, int VEC_, int OCC_>
+// One lane's fragment reads for one group of 8 values of k (k0 .. k0+7):
+// the four values k0 + 4h .. k0 + 4h + 3 of row (A) or column (B) l32 of
+// the tile.  `tile` points at the operand's element (mn0, 0) in its own
+// storage order; reads outside rows/columns [0, mn_valid) or past ke give 0.
+template <bool KC, int VEC>
+struct SmallOperand {
+    uint32_t lane_off[4];  // byte offsets of the lane's four values from (mn0, k0)
+
+    __device__ __forceinline__ void init(int64_t ld, int mn_valid, int l32, int half)
+    {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int64_t o = KC ? l32 * ld + 4 * half + s : (4 * half + s) * ld + l32;
+            lane_off[s] = l32 < mn_valid ? (uint32_t)(o * 4) : kOutside;
+        }
+    }
+
+    __device__ __forceinline__ f32x4 load(const float *tile, int64_t ld, int k0, int ke, int K,
+                                          int mn_valid, int half) const
+    {
+        f32x4 v;
+        if constexpr (KC) {
+            // k runs along the row: only this wavefront's range may be read
+            const __amdgpu_buffer_rsrc_t r =
+                small_buffer(tile + k0, ((int64_t)(mn_valid - 1) * ld + (K - k0)) * 4);
+            if constexpr (VEC == 4) {
+                const uint32_t o = k0 + 4 * half < ke ? lane_off[0] : kOutside;
+                v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint32_t o = k0 + 4 * half + s < ke ? lane_off[s] : kOutside;
+                    v[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+                }
+            }
+        } else {
+            // k runs down the rows: rows >= ke lie past the extent
+            const __amdgpu_buffer_rsrc_t r =
+                small_buffer(tile + (int64_t)k0 * ld, ((int64_t)(ke - k0 - 1) * ld + mn_valid) * 4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t o = lane_off[s];
+                v[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0));
+            }
+        }
+        return v;
+    }
+};
+
+template <int KS_, int D_, int VEC_, int OCC_, bool TA_, bool TB_>
 struct SmallCfg {
     static constexpr int KS = KS_, D = D_, VEC = VEC_, OCC = OCC_;
+    static constexpr bool TA = TA_, TB = TB_;
     static constexpr int NT = kWave * KS;
 };
 
@@ -51,6 +105,7 @@ void mfma_sgemm_small_kernel(int M, int N, int K, const float *__restrict__ A, i
                              int64_t ldc)
 {
     constexpr int KS = G::KS, D = G::D, VEC = G::VEC;
+    constexpr bool A_KC = !G::TA, B_KC = G::TB;
     __shared__ float part[KS][16 * kWave];
 
     const int tiles_m = (M + 31) / 32, tiles_n = (N + 31) / 32;
@@ -68,40 +123,20 @@ void mfma_sgemm_small_kernel(int M, int N, int K, const float *__restrict__ A, i
     const int kb = min(K, w * chunk), ke = min(K, kb + chunk);
     const int groups = (ke - kb + 7) / 8;
 
-    // lane offsets (bytes) from a group's first element
-    const uint32_t a_lane = l32 < rows_valid ? (uint32_t)((l32 * lda + 4 * half) * 4) : kOutside;
-    uint32_t b_lane[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        b_lane[s] = l32 < cols_valid ? (uint32_t)(((4 * half + s) * ldb + l32) * 4) : kOutside;
-    const float *a_tile = A + (int64_t)m0 * lda;
-    const float *b_tile = B + n0;
+    SmallOperand<A_KC, VEC> oa;
+    SmallOperand<B_KC, VEC> ob;
+    oa.init(lda, rows_valid, l32, half);
+    ob.init(ldb, cols_valid, l32, half);
+    const float *a_tile = A + (A_KC ? (int64_t)m0 * lda : (int64_t)m0);
+    const float *b_tile = B + (B_KC ? (int64_t)n0 * ldb : (int64_t)n0);
 
-    f32x4 a_ring[D];
-    float b_ring[D][4];
-    // Issue the reads of group g (k0 = kb + 8g) into ring slot `slot`.
+    f32x4 a_ring[D], b_ring[D];
+    // Issue the reads of group g (k0 = kb + 8g) into ring slot `slot`; past
+    // the wavefront's range they read zero.
     auto issue = [&] __device__(int g, int slot) {
         const int k0 = kb + 8 * g;
-        const __amdgpu_buffer_rsrc_t ra =
-            small_buffer(a_tile + k0, ((int64_t)(rows_valid - 1) * lda + (K - k0)) * 4);
-        const __amdgpu_buffer_rsrc_t rb =
-            small_buffer(b_tile + (int64_t)k0 * ldb, ((int64_t)(ke - k0 - 1) * ldb + cols_valid) * 4);
-        const bool a_in = k0 + 4 * half < ke;  // past ke: another wavefront's k (or past K)
-        if constexpr (VEC == 4) {
-            const uint32_t off = a_in ? a_lane : kOutside;
-            a_ring[slot] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t off = (k0 + 4 * half + s < ke) ? a_lane + 4 * s : kOutside;
-                a_ring[slot][s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, off, 0, 0));
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint32_t off = b_lane[s];
-            b_ring[slot][s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
-        }
+        a_ring[slot] = oa.load(a_tile, lda, k0, ke, K, rows_valid, half);
+        b_ring[slot] = ob.load(b_tile, ldb, k0, ke, K, cols_valid, half);
     };
 
     f32x16 acc = f32x16(0.0f);
@@ -147,23 +182,44 @@ hipError_t launch_small(const GemmArgs &g, hipStream_t stream)
                            dim3((unsigned)tiles), dim3(G::NT), args, 0, stream);
 }
 
-//                KS  D VEC OCC
-typedef SmallCfg<4, 4, 4, 4> S4D4v4;
-typedef SmallCfg<8, 8, 4, 4> S8D8v4;
-typedef SmallCfg<4, 4, 1, 4> S4D4v1;
-typedef SmallCfg<8, 8, 1, 4> S8D8v1;
+// One split in its four operand orders (NN, TN, NT, TT).
+template <int KS, int D, int VEC, int OCC>
+struct Split {
+    template <bool TA, bool TB>
+    using C = SmallCfg<KS, D, VEC, OCC, TA, TB>;
+    static hipError_t launch(const GemmArgs &g, hipStream_t stream)
+    {
+        switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
+            case 0: return launch_small<C<false, false>>(g, stream);
+            case 1: return launch_small<C<true, false>>(g, stream);
+            case 2: return launch_small<C<false, true>>(g, stream);
+            default: return launch_small<C<true, true>>(g, stream);
+        }
+    }
+};
 
-// Offsets span 32 rows of A and 8 rows of B.
-constexpr int64_t kMaxLda = ((((int64_t)1 << 31) - 16) / 4) / 32;
-constexpr int64_t kMaxLdb = ((((int64_t)1 << 31) - 16) / 4 - 32) / 8;
+//            KS  D VEC OCC
+typedef Split<4, 4, 4, 4> S4D4v4;
+typedef Split<8, 8, 4, 4> S8D8v4;
+typedef Split<4, 4, 1, 4> S4D4v1;
+typedef Split<8, 8, 1, 4> S8D8v1;
+
+// Offsets span 32 rows of a k-contiguous operand and 8 rows of an
+// mn-contiguous one.
+constexpr int64_t kMaxLdKc = ((((int64_t)1 << 31) - 16) / 4 - 8) / 32;
+constexpr int64_t kMaxLdMc = ((((int64_t)1 << 31) - 16) / 4 - 32) / 8;
 
 // bk = 8·KS: the K granularity of a work-group.  Efficiencies and the fixed
 // cost per round measured on MI355X (shapes 128 to 1024 on a side, K to 8192).
 const MfmaVariant kSmallVariants[] = {
-    {"m32n32k8_s4d4_vec4", 32, 32, 32, 4, 4, kMaxLda, kMaxLdb, 0.25, 0.38, 6400.0, &launch_small<S4D4v4>},
-    {"m32n32k8_s8d8_vec4", 32, 32, 64, 4, 2, kMaxLda, kMaxLdb, 0.36, 0.40, 12000.0, &launch_small<S8D8v4>},
-    {"m32n32k8_s4d4_vec1", 32, 32, 32, 1, 4, kMaxLda, kMaxLdb, 0.20, 0.30, 6400.0, &launch_small<S4D4v1>},
-    {"m32n32k8_s8d8_vec1", 32, 32, 64, 1, 2, kMaxLda, kMaxLdb, 0.28, 0.32, 12000.0, &launch_small<S8D8v1>},
+    {"m32n32k8_s4d4_vec4", 32, 32, 32, 4, 4, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.25, 0.38, 6400.0,
+     &S4D4v4::launch},
+    {"m32n32k8_s8d8_vec4", 32, 32, 64, 4, 2, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.36, 0.40, 12000.0,
+     &S8D8v4::launch},
+    {"m32n32k8_s4d4_vec1", 32, 32, 32, 1, 4, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.20, 0.30, 6400.0,
+     &S4D4v1::launch},
+    {"m32n32k8_s8d8_vec1", 32, 32, 64, 1, 2, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.28, 0.32, 12000.0,
+     &S8D8v1::launch},
 };
 
 }  // namespace

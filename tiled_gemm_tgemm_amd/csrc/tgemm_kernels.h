@@ -9,6 +9,9 @@
 
 namespace tgemm {
 
+// op(A) is M×K and op(B) is K×N.  trans_a: A is stored K×M (op(A) = Aᵀ),
+// element (i, k) at A[k*lda + i]; otherwise at A[i*lda + k].  trans_b: B is
+// stored N×K, element (k, j) at B[j*ldb + k]; otherwise at B[k*ldb + j].
 struct GemmArgs {
     int M, N, K;
     const float *A;
@@ -17,6 +20,7 @@ struct GemmArgs {
     int64_t ldb;
     float *C;
     int64_t ldc;
+    bool trans_a = false, trans_b = false;
 };
 
 // One thread per output, 16×16 blocks.
@@ -34,8 +38,11 @@ struct MfmaVariant {
     int bm, bn, bk;      // macro tile and phase depth
     int vec;             // 4: 16-byte loads (alignment required), 1: 4-byte loads
     int wg_per_cu;       // work-groups one compute unit holds at once
-    int64_t max_lda;     // largest leading dimensions the configuration takes
-    int64_t max_ldb;
+    int64_t max_lda;     // largest leading dimensions the configuration takes,
+    int64_t max_ldb;     // operands as stored ...
+    int64_t max_lda_t;   // ... and transposed
+    int64_t max_ldb_t;
+    bool trans;          // takes transposed operands
     // Measured fraction of the matrix-core rate a work-group sustains when it
     // is alone on its compute unit, and when wg_per_cu of them share it; plus
     // a fixed cost per round of work-groups (SIMD cycles).  Used only to rank
