@@ -30,7 +30,8 @@
  *             failed.  A fault inside a kernel shows up at the caller's next
  *             stream synchronisation, as for any asynchronous HIP work.
  *             Nothing is printed and no C++ exception crosses this interface.
- * Sizes       M, N, K up to 2^31 - 1; element offsets are 64-bit.
+ * Sizes       M, N, K up to 2^31 - 2^16 (TGEMM_ERROR_NOT_SUPPORTED above);
+ *             element offsets are 64-bit.
  * Threads     All entry points are re-entrant and may be called concurrently
  *             on different streams.
  * Rounding    The tiled MFMA kernels sum in an order of their own; for real
@@ -61,7 +62,7 @@ typedef enum tgemm_op {
 typedef enum tgemm_status {
     TGEMM_SUCCESS = 0,
     TGEMM_ERROR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer or overlap */
-    TGEMM_ERROR_NOT_SUPPORTED = 2, /* a size above 2^31-1, or an unknown kernel choice */
+    TGEMM_ERROR_NOT_SUPPORTED = 2, /* a size above 2^31-2^16, or an unknown kernel choice */
     TGEMM_ERROR_HIP = 3            /* the HIP runtime refused the launch */
 } tgemm_status_t;
 
@@ -167,6 +168,21 @@ tgemm_status_t tgemm_sgemm_lds(int64_t M, int64_t N, int64_t K,
                                const float *A, int64_t lda,
                                const float *B, int64_t ldb,
                                float *C, int64_t ldc, int tile, int pad, hipStream_t stream);
+
+/*
+ * Ablation 3 — the tiled kernel with more work per thread (page 1, end of
+ * section [Shared Memory], "Tile Size 결정": let each thread compute several
+ * outputs to use more on-chip memory), on the vector ALUs: 256 threads per
+ * 128×128 tile, an 8×8 block of outputs per thread in registers, phases of 8
+ * values of k staged through LDS (A transposed on the way in, page 1 section
+ * [Coalescing], "Corner Turning"), two LDS stages, one barrier per phase.
+ * Every output is one fused multiply-add chain in ascending k, so the result
+ * equals tgemm_sgemm_naive's bit for bit.  Arguments and errors as above.
+ */
+tgemm_status_t tgemm_sgemm_simt(int64_t M, int64_t N, int64_t K,
+                                const float *A, int64_t lda,
+                                const float *B, int64_t ldb,
+                                float *C, int64_t ldc, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *tgemm_status_string(tgemm_status_t status);

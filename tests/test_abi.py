@@ -71,11 +71,13 @@ def test_static_queries(lib):
 # case below is rejected (or finishes as a no-op) before any HIP call.
 A_, B_, C_ = 0x10000000, 0x20000000, 0x30000000
 INVALID, UNSUPPORTED = tg.TGEMM_ERROR_INVALID_VALUE, tg.TGEMM_ERROR_NOT_SUPPORTED
+MAX_DIM = 2 ** 31 - 2 ** 16  # largest M, N, K the header allows
 
 ENTRY = {
     "sgemm": lambda *a: tg.tgemm_sgemm(*a, None),
     "naive": lambda *a: tg.tgemm_sgemm_naive(*a, None),
     "lds": lambda *a: tg.tgemm_sgemm_lds(*a, 16, 1, None),
+    "simt": lambda *a: tg.tgemm_sgemm_simt(*a, None),
     "mfma": lambda *a: tg.tgemm_sgemm_mfma(*a, 0, None),
 }
 
@@ -96,6 +98,10 @@ CASES = [
     ((4, 4, 4, A_, 4, B_, 4, B_ + 60, 4), INVALID),  # C overlaps B's last element
     ((2 ** 31, 4, 4, A_, 4, B_, 4, C_, 4), UNSUPPORTED),
     ((4, 4, 2 ** 31, A_, 2 ** 31, B_, 4, C_, 4), UNSUPPORTED),
+    ((MAX_DIM + 1, 4, 4, A_, 4, B_, 4, C_, 4), UNSUPPORTED),       # largest size + 1
+    ((0, 4, MAX_DIM + 1, A_, MAX_DIM + 1, B_, 4, C_, 4), UNSUPPORTED),
+    ((0, 4, MAX_DIM, A_, MAX_DIM, B_, 4, C_, 4), tg.TGEMM_SUCCESS),  # largest K, M = 0
+    ((4, 0, MAX_DIM, A_, MAX_DIM, B_, 1, C_, 1), tg.TGEMM_SUCCESS),
     ((0, 4, 4, A_, 4, B_, 4, C_, 4), tg.TGEMM_SUCCESS),  # M = 0: nothing to do
     ((4, 0, 4, A_, 4, B_, 1, C_, 1), tg.TGEMM_SUCCESS),  # N = 0
     ((0, 4, 4, 0, 4, 0, 4, 0, 4), tg.TGEMM_SUCCESS),     # no-op ignores pointers

@@ -135,6 +135,8 @@ def test_square512_uniform_all_kernels():
         log(f"{w.name}: lds tile={tile} pad={pad}")
         C = run(A, B, "lds", tile=tile, pad=pad)
         assert np.array_equal(C, fma), f"lds{tile} pad{pad} differs from the fma model"
+    log(f"{w.name}: simt")
+    assert np.array_equal(run(A, B, "simt"), fma), "simt differs from the sequential fma model"
 
 
 def test_square1024_int4_bit_exact():
@@ -152,6 +154,7 @@ def test_square1024_int4_bit_exact():
     assert_exact(run(A, B, "naive"), Pi, "naive")
     assert_exact(run(A, B, "lds", tile=16, pad=1), Pi, "lds16")
     assert_exact(run(A, B, "lds", tile=32, pad=0), Pi, "lds32")
+    assert_exact(run(A, B, "simt"), Pi, "simt")
 
 
 def test_rect3000x1000x5000_normal_masked_edges():
@@ -227,6 +230,7 @@ def test_edge_shapes_integer_exact(M, N, K):
             continue
         assert_exact(run(A, B, "mfma", variant=v), Pi, name)
     assert_exact(run(A, B, "naive"), Pi, "naive")
+    assert_exact(run(A, B, "simt"), Pi, "simt")
     for tile in (2, 16, 32) if max(M, N) <= 64 else (16, 32):
         assert_exact(run(A, B, "lds", tile=tile, pad=1), Pi, f"lds{tile}")
 
@@ -258,7 +262,7 @@ def test_guard_bands(M, N, K, pad):
     Pi = oracle.gemm_i64(A, B)
     kernels = [("auto", {})] + [("mfma", {"variant": v}) for v, n in enumerate(variants())
                                 if runnable(n, M, N, K) and ("vec1" in n or pad % 4 == 0)]
-    kernels += [("naive", {}), ("lds", {"tile": 16, "pad": 1})]
+    kernels += [("naive", {}), ("lds", {"tile": 16, "pad": 1}), ("simt", {})]
     for kernel, kw in kernels:
         log(f"guard {M}x{N}x{K} pad {pad}: {kernel} {kw}")
         _, Av = guarded(A, 3, pad, float("nan"))
@@ -308,6 +312,44 @@ def test_leading_dimension_beyond_buffer_offsets():
         assert (st == tg.TGEMM_SUCCESS) == name.endswith("_flat"), name
     torch.cuda.synchronize()
     del big
+
+
+def test_largest_k():
+    """K at the largest size the interface takes (2^31 - 2^16), M = N = 1, A
+    stored transposed (K×1): one dot product of random ±1 values through the
+    split-K configuration tgemm_sgemm picks.  Every partial sum any kernel can
+    form is a sum of at most K independent ±1 terms, far below 2^24 in
+    magnitude (Hoeffding), so float32 sums are exact.  With the values drawn
+    as bits (1 -> +1, 0 -> -1) the exact dot product is K - 2·popcount(a xor b)."""
+    K = 2 ** 31 - 2 ** 16
+    rng = np.random.default_rng(20)
+    pa = np.frombuffer(bytearray(rng.bytes(K // 8)), np.uint8)
+    pb = np.frombuffer(bytearray(rng.bytes(K // 8)), np.uint8)
+    want = K - 2 * int(np.bitwise_count(np.bitwise_xor(pa, pb)).sum(dtype=np.int64))
+
+    def unpack(packed):  # bit b of byte i -> element 8i + b, as ±1 in float32
+        bits = (torch.from_numpy(packed).to("cuda").unsqueeze(1) >>
+                torch.arange(8, dtype=torch.uint8, device="cuda")) & 1
+        x = bits.reshape(K, 1).float()
+        del bits
+        return x.mul_(2).sub_(1)
+
+    log(f"largest K = {K}")
+    dA, dB = unpack(pa), unpack(pb)  # both stored K×1
+    C = torch.full((1, 1), float("nan"), device="cuda")
+    v = tg.tgemm_sgemm_variant_for_ex(tg.TGEMM_OP_T, tg.TGEMM_OP_N, 1, 1, K, dA.data_ptr(), 1,
+                                      dB.data_ptr(), 1, C.data_ptr(), 1)
+    log(f"largest K: {variants()[v]}")
+    st = tg.tgemm_sgemm_ex(tg.TGEMM_OP_T, tg.TGEMM_OP_N, 1, 1, K, dA.data_ptr(), 1, dB.data_ptr(), 1,
+                           C.data_ptr(), 1, None)
+    assert st == tg.TGEMM_SUCCESS
+    torch.cuda.synchronize()
+    assert C.item() == want
+    st = tg.tgemm_sgemm_ex(tg.TGEMM_OP_T, tg.TGEMM_OP_N, 1, 1, K + 1, dA.data_ptr(), 1, dB.data_ptr(), 1,
+                           C.data_ptr(), 1, None)
+    assert st == tg.TGEMM_ERROR_NOT_SUPPORTED
+    del dA, dB
+    torch.cuda.empty_cache()
 
 
 OPS = [(True, False), (False, True), (True, True)]
@@ -431,7 +473,7 @@ def test_transpose_symmetry():
 
 def test_invariants_scaling_sign_determinism():
     A, B, _ = wl.random_matrices(320, 288, 264, "uniform", 91)
-    for kernel, kw in [("auto", {}), ("naive", {}), ("lds", {"tile": 16, "pad": 1})] + \
+    for kernel, kw in [("auto", {}), ("naive", {}), ("lds", {"tile": 16, "pad": 1}), ("simt", {})] + \
             [("mfma", {"variant": v}) for v in range(len(variants()))]:
         log(f"invariants {kernel} {kw}")
         C = run(A, B, kernel, **kw)
@@ -450,6 +492,7 @@ def test_worked_example_tile2():
     for pad in (0, 1):
         assert np.array_equal(run(Mx, Nx, "lds", tile=2, pad=pad), want)
     assert np.array_equal(run(Mx, Nx, "naive"), want)
+    assert np.array_equal(run(Mx, Nx, "simt"), want)
     for v, name in enumerate(variants()):
         assert np.array_equal(run(Mx, Nx, "mfma", variant=v), want), name
 
@@ -496,7 +539,7 @@ def test_graph_capture_replays():
 # ------------------------------------------------------------ ABI on the device
 
 def test_zero_k_fills_positive_zero_and_empty_is_noop():
-    for kernel, kw in [("auto", {}), ("naive", {}), ("lds", {"tile": 16, "pad": 0}),
+    for kernel, kw in [("auto", {}), ("naive", {}), ("lds", {"tile": 16, "pad": 0}), ("simt", {}),
                        ("mfma", {"variant": 0})]:
         C = torch.full((5, 12), float("nan"), device="cuda")
         tg.sgemm(torch.empty((5, 0), device="cuda"), torch.empty((0, 12), device="cuda"), out=C,

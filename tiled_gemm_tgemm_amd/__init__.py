@@ -30,12 +30,13 @@ from ._lib import (  # noqa: F401
     tgemm_sgemm_mfma_ex,
     tgemm_sgemm_variant_for_ex,
     tgemm_sgemm_naive,
+    tgemm_sgemm_simt,
     tgemm_sgemm_variant_for,
     tgemm_status_string,
     tgemm_version,
 )
 
-KERNELS = ("auto", "mfma", "naive", "lds")
+KERNELS = ("auto", "mfma", "naive", "lds", "simt")
 
 
 def _check(t, name):
@@ -67,8 +68,8 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
     no copy.  `out` must be row-major.
     kernel: "auto" (tgemm_sgemm_ex), "mfma" (tgemm_sgemm_mfma_ex with
     `variant`; without one it is "auto"), "naive" (tgemm_sgemm_naive) or
-    "lds" (tgemm_sgemm_lds with tile/pad) — the last two for row-major
-    operands only.  The call is queued on `stream` (default: torch's current
+    "lds" (tgemm_sgemm_lds with tile/pad) or "simt" (tgemm_sgemm_simt) — the
+    last three for row-major operands only.  The call is queued on `stream` (default: torch's current
     stream) and returns `out` without waiting.
     """
     import torch
@@ -93,7 +94,7 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc)
-    if kernel in ("naive", "lds") and (op_a, op_b) != (TGEMM_OP_N, TGEMM_OP_N):
+    if kernel in ("naive", "lds", "simt") and (op_a, op_b) != (TGEMM_OP_N, TGEMM_OP_N):
         raise ValueError(f"the {kernel} kernel takes row-major operands only")
     if kernel == "auto" or (kernel == "mfma" and variant is None):
         st = tgemm_sgemm_ex(op_a, op_b, *args, stream)
@@ -103,6 +104,8 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
         st = tgemm_sgemm_naive(*args, stream)
     elif kernel == "lds":
         st = tgemm_sgemm_lds(*args, tile, pad, stream)
+    elif kernel == "simt":
+        st = tgemm_sgemm_simt(*args, stream)
     else:
         raise ValueError(f"kernel must be one of {KERNELS}")
     if st != TGEMM_SUCCESS:

@@ -37,6 +37,7 @@ SIGNATURES = {
     "tgemm_sgemm_variant_for": (ctypes.c_int, _GEMM),
     "tgemm_sgemm_naive": (ctypes.c_int, _GEMM + [_ptr]),
     "tgemm_sgemm_lds": (ctypes.c_int, _GEMM + [ctypes.c_int, ctypes.c_int, _ptr]),
+    "tgemm_sgemm_simt": (ctypes.c_int, _GEMM + [_ptr]),
     "tgemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tgemm_version": (ctypes.c_int, []),
 }
@@ -94,6 +95,10 @@ def tgemm_sgemm_naive(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def tgemm_sgemm_lds(M, N, K, A, lda, B, ldb, C, ldc, tile, pad, stream=None) -> int:
     return library().tgemm_sgemm_lds(M, N, K, A, lda, B, ldb, C, ldc, tile, pad, stream)
+
+
+def tgemm_sgemm_simt(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return library().tgemm_sgemm_simt(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def tgemm_mfma_variant_count() -> int:

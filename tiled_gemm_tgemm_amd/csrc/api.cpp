@@ -13,7 +13,10 @@ namespace {
 
 using tgemm::GemmArgs;
 
-constexpr int64_t kMaxDim = 0x7fffffff;
+// Largest M, N or K: 2^31 - 2^16, so that every kernel's tile and phase
+// counts, and the k index of a phase rounded up to its depth, stay within
+// 32-bit integers.
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - ((int64_t)1 << 16);
 
 int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
@@ -238,12 +241,23 @@ tgemm_status_t tgemm_sgemm_lds(int64_t M, int64_t N, int64_t K, const float *A, 
     return from_hip(tgemm::launch_lds_tiled(pack(false, false, M, N, K, A, lda, B, ldb, C, ldc), tile, pad, stream));
 }
 
+tgemm_status_t tgemm_sgemm_simt(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                                const float *B, int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
+{
+    Quick quick;
+    const tgemm_status_t st = validate(false, false, M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if ((M + 127) / 128 > 65535) return TGEMM_ERROR_NOT_SUPPORTED;  // grid rows limit
+    return from_hip(tgemm::launch_simt_tiled(pack(false, false, M, N, K, A, lda, B, ldb, C, ldc), stream));
+}
+
 const char *tgemm_status_string(tgemm_status_t status)
 {
     switch (status) {
         case TGEMM_SUCCESS: return "success";
         case TGEMM_ERROR_INVALID_VALUE: return "invalid value (size, leading dimension, pointer or overlap)";
-        case TGEMM_ERROR_NOT_SUPPORTED: return "not supported (size above 2^31-1, alignment, or unknown kernel choice)";
+        case TGEMM_ERROR_NOT_SUPPORTED: return "not supported (size above 2^31-2^16, alignment, or unknown kernel choice)";
         case TGEMM_ERROR_HIP: return "HIP runtime refused the launch";
     }
     return "unknown status";

@@ -29,6 +29,9 @@ hipError_t launch_naive(const GemmArgs &g, hipStream_t stream);
 // The two-barrier shared-memory tiled kernel; tile in {2, 8, 16, 32}, pad in {0, 1}.
 hipError_t launch_lds_tiled(const GemmArgs &g, int tile, int pad, hipStream_t stream);
 
+// 128×128 tiles, 8×8 outputs per thread on the vector ALUs.
+hipError_t launch_simt_tiled(const GemmArgs &g, hipStream_t stream);
+
 // C(i,j) = +0 for i < M, j < N (the empty sum, K = 0).
 hipError_t launch_fill_zero(int M, int N, float *C, int64_t ldc, hipStream_t stream);
 
