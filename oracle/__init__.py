@@ -16,7 +16,9 @@ file only marshals numpy arrays.  Definitions followed, all on page 1
 * ``gemm_fma_f32``: the register accumulator of the pages' kernels (sections
   [Matrix Multiplication] "sum" loop and [Shared Memory] Pvalue loop), one
   float32 fused multiply-add per k in ascending order;
-* ``checksums``: row/column sums of the product, formed without the product.
+* ``checksums``: row/column sums of the product, formed without the product;
+* ``transpose``: page 2 ("Lec 29 · GPU Architecture (2)"), §1.4 — element
+  (i, j) of the input moves to (j, i) of the output, as a 32-bit word.
 
 Pins (what ties these to something other than themselves) are in
 ``tests/test_oracle_pins.py``.  The structural models of the pages' kernels
@@ -37,6 +39,7 @@ _lib = None
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_u32p = np.ctypeslib.ndpointer(dtype=np.uint32, flags="C_CONTIGUOUS")
 _i64 = ctypes.c_int64
 
 
@@ -58,6 +61,8 @@ def _load():
     lib.oracle_checksums.restype = ctypes.c_int
     lib.oracle_checksums.argtypes = [_i64, _i64, _i64, _f32p, _i64, _f32p, _i64,
                                      _f64p, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_transpose.restype = ctypes.c_int
+    lib.oracle_transpose.argtypes = [_i64, _i64, _u32p, _i64, _u32p, _i64]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -148,6 +153,19 @@ def checksums(A, B, lib=None):
     _check(lib.oracle_checksums(M, N, K, A, A.shape[1], B, B.shape[1],
                                 row, rowabs, col, colabs, work), "oracle_checksums")
     return row[:M], rowabs[:M], col[:N], colabs[:N]
+
+
+def transpose(A, lib=None):
+    """Aᵀ of a 2-D float32 array (N×M for M×N), every element's bits unchanged."""
+    lib = lib or _load()
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    if A.ndim != 2:
+        raise ValueError(f"transpose needs a 2-D array, got shape {A.shape}")
+    M, N = A.shape
+    src = A.view(np.uint32) if A.size else np.zeros((max(M, 1), max(N, 1)), np.uint32)
+    out = np.empty((max(N, 1), max(M, 1)), np.uint32)
+    _check(lib.oracle_transpose(M, N, src, src.shape[1], out, out.shape[1]), "oracle_transpose")
+    return out[:N, :M].view(np.float32)
 
 
 def num_threads(lib=None) -> int:

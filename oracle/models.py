@@ -20,6 +20,10 @@ GPU product path imports this.  Pure Python loops; meant for small inputs.
   4-byte words, consecutive words in consecutive banks; several threads
   touching different words of one bank are serialised, the same word is a
   broadcast).
+* ``transpose_run``: the transpose kernels of page 2 §1.4 (naive, and tiled
+  through shared memory with optional padding), thread by thread, recording
+  the addresses each warp instruction touches; ``bursts`` counts the DRAM
+  burst sections such an instruction needs (page 2 §1.4, DRAM bursts).
 
 All three kernels' models assume what the pages assume: square Width×Width
 matrices with Width a multiple of the tile (page 1, "Kernel 호출").
@@ -141,3 +145,68 @@ def conflict_degree(word_addresses, nbanks: int = 32) -> int:
     for w in word_addresses:
         per_bank[w % nbanks].add(w)
     return max((len(s) for s in per_bank.values()), default=0)
+
+
+def bursts(byte_addresses, burst_bytes: int = 32) -> int:
+    """Number of burst-aligned sections of `burst_bytes` that one warp
+    instruction's accesses (4-byte words at these byte addresses) touch;
+    a fully coalesced access of 32 words touches 128 / 32 = 4."""
+    return len({a // burst_bytes for a in byte_addresses})
+
+
+def transpose_run(M, N, kind: str, tile: int = 32, rows: int = 8, pad: int = 0, warp: int = 32):
+    """Run a transpose kernel of page 2 §1.4 on an M×N matrix of distinct
+    values, thread by thread.
+
+    Blocks of tile×rows threads each own a tile×tile tile; thread (tx, ty)
+    handles the elements of rows ty, ty + rows, ... of the tile (the page's
+    loop over j).  "naive": read input (y, x), write output (x, y) directly.
+    "tiled": read input (y, x) into tile[ty + j][tx]; all threads wait; with
+    the block offsets swapped, write output row (x0 + ty + j), column
+    (y0 + tx) from tile[tx][ty + j].  pad adds words to each tile row.
+
+    Returns {"B": the output as nested lists, "reads"/"writes": one list of
+    byte addresses per warp instruction (row-major, 4-byte elements, leading
+    dimensions N and M), "lds_reads": one list of tile word indices per warp
+    instruction that reads the tile}.  Assumes M, N multiples of tile.
+    """
+    assert kind in ("naive", "tiled") and M % tile == 0 and N % tile == 0 and tile % rows == 0
+    A = [[i * N + j for j in range(N)] for i in range(M)]
+    B = [[None] * M for _ in range(N)]
+    reads, writes, lds_reads = [], [], []
+    nthreads = tile * rows
+    for by in range(M // tile):
+        for bx in range(N // tile):
+            x0, y0 = bx * tile, by * tile
+            tile_words = {}
+            for j in range(0, tile, rows):
+                # one instruction per warp: threads t = ty*tile + tx, in warps of `warp`
+                for w0 in range(0, nthreads, warp):
+                    rd, wr = [], []
+                    for t in range(w0, w0 + warp):
+                        tx, ty = t % tile, t // tile
+                        y, x = y0 + ty + j, x0 + tx
+                        rd.append(4 * (y * N + x))
+                        if kind == "naive":
+                            B[x][y] = A[y][x]
+                            wr.append(4 * (x * M + y))
+                        else:
+                            tile_words[(ty + j) * (tile + pad) + tx] = A[y][x]
+                    reads.append(rd)
+                    if wr:
+                        writes.append(wr)
+            if kind == "tiled":
+                # (barrier) then the write-out, block offsets swapped
+                for j in range(0, tile, rows):
+                    for w0 in range(0, nthreads, warp):
+                        wr, lr = [], []
+                        for t in range(w0, w0 + warp):
+                            tx, ty = t % tile, t // tile
+                            word = tx * (tile + pad) + ty + j
+                            r, c = x0 + ty + j, y0 + tx
+                            B[r][c] = tile_words[word]
+                            wr.append(4 * (r * M + c))
+                            lr.append(word)
+                        writes.append(wr)
+                        lds_reads.append(lr)
+    return {"A": A, "B": B, "reads": reads, "writes": writes, "lds_reads": lds_reads}

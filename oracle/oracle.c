@@ -18,6 +18,10 @@
  * are shared out across OpenMP threads; each element is still one plain
  * sequential sum, so the thread count never changes a result.
  *
+ * Also the transpose of page 2 ("Lec 29 · GPU Architecture (2)"), §1.4:
+ * element (i, j) of the input becomes element (j, i) of the output, copied
+ * as a 32-bit word (no arithmetic at all).
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math), see build.py.
  */
 #include <math.h>
@@ -196,6 +200,22 @@ int oracle_checksums(int64_t M, int64_t N, int64_t K,
         if (col) col[j] = c;
         if (colabs) colabs[j] = ca;
     }
+    return ORACLE_OK;
+}
+
+/*
+ * Transpose (page 2 §1.4): B(j, i) = A(i, j) for i < M, j < N.  A is M×N
+ * with leading dimension lda >= max(1, N), B is N×M with ldb >= max(1, M);
+ * both row-major.  Elements are moved as 32-bit words, so every bit pattern
+ * (signed zeros, NaN payloads, subnormals) arrives unchanged.  Nothing of B
+ * outside its N×M elements is written.
+ */
+int oracle_transpose(int64_t M, int64_t N, const uint32_t *A, int64_t lda, uint32_t *B, int64_t ldb)
+{
+    if (M < 0 || N < 0 || lda < (N > 1 ? N : 1) || ldb < (M > 1 ? M : 1)) return ORACLE_BAD_ARGS;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) B[j * ldb + i] = A[i * lda + j];
     return ORACLE_OK;
 }
 

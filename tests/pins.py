@@ -11,6 +11,7 @@ IEEE-754 definition of round-to-nearest-even.
 from __future__ import annotations
 
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -291,9 +292,85 @@ def pin_empty(lib):
     return None
 
 
+# ---------------------------------------------------------------- transpose
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TRANSPOSE_SHAPES = [(1, 1), (1, 17), (17, 1), (3, 4), (33, 65), (64, 64), (100, 7)]
+
+
+def _bits(x):
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def pin_transpose_golden(lib):
+    """The hand-written 3x4 example of tests/golden/transpose_3x4.txt (page 2 §1.4)."""
+    rows = {"in": [], "out": []}
+    with open(os.path.join(GOLDEN, "transpose_3x4.txt")) as f:
+        for line in f:
+            parts = line.split()
+            if parts and parts[0] in rows:
+                rows[parts[0]].append([float(v) for v in parts[1:]])
+    A = np.array(rows["in"], np.float32)
+    want = np.array(rows["out"], np.float32)
+    if not np.array_equal(_bits(oracle.transpose(A, lib=lib)), _bits(want)):
+        return "golden 3x4 transpose differs (bitwise)"
+    return None
+
+
+def pin_transpose_closed_form(lib):
+    """A(i, j) = i·N + j (exact in float32): the output at (j, i) must hold i·N + j."""
+    for M, N in TRANSPOSE_SHAPES + [(0, 5), (5, 0)]:
+        A = (np.arange(M)[:, None] * N + np.arange(N)[None, :]).astype(np.float32)
+        B = oracle.transpose(A, lib=lib)
+        want = (np.arange(M)[None, :] * N + np.arange(N)[:, None]).astype(np.float32)
+        if B.shape != (N, M) or not np.array_equal(B, want):
+            return f"closed form fails at {M}x{N}"
+    return None
+
+
+def pin_transpose_library_and_bits(lib):
+    """Equal, bit for bit, to numpy's own transpose copy, on values that include
+    NaNs with payloads, ±0, ±inf and subnormals; applying it twice gives A back."""
+    rng = np.random.default_rng(44)
+    for M, N in TRANSPOSE_SHAPES:
+        words = rng.integers(0, 2 ** 32, size=(M, N), dtype=np.uint64).astype(np.uint32)
+        special = np.array([0x7FC01234, 0xFFA00001, 0x80000000, 0x00000000, 0x7F800000,
+                            0xFF800000, 0x00000001, 0x807FFFFF], np.uint32)
+        flat = words.reshape(-1)
+        flat[: min(flat.size, special.size)] = special[: flat.size]
+        A = words.view(np.float32)
+        B = oracle.transpose(A, lib=lib)
+        if not np.array_equal(_bits(B), np.ascontiguousarray(words.T)):
+            return f"differs from numpy's transpose at {M}x{N}"
+        if not np.array_equal(_bits(oracle.transpose(B, lib=lib)), words):
+            return f"twice is not the identity at {M}x{N}"
+    return None
+
+
+def pin_transpose_strides(lib):
+    """Leading dimensions wider than the rows: padding of A is never read (NaN
+    there would not show, so it holds values that would) and padding of B is
+    never written."""
+    lib_ = lib or oracle._load()
+    for M, N, pa, pb in [(3, 4, 3, 5), (17, 1, 2, 1), (1, 9, 0, 4), (20, 30, 7, 2)]:
+        lda, ldb = N + pa, M + pb
+        Abuf = np.full((M, lda), 7.0, np.float32)
+        Abuf[:, :N] = (np.arange(M)[:, None] * N + np.arange(N)[None, :])
+        Bbuf = np.full((N, ldb), -3.0, np.float32)
+        rc = lib_.oracle_transpose(M, N, Abuf.view(np.uint32), lda, Bbuf.view(np.uint32), ldb)
+        if rc != 0:
+            return f"rejected lda={lda}, ldb={ldb}"
+        if not np.array_equal(Bbuf[:, :M], Abuf[:, :N].T):
+            return f"wrong values with lda={lda}, ldb={ldb}"
+        if np.any(Bbuf[:, M:] != -3.0):
+            return f"wrote B's padding with ldb={ldb}"
+    return None
+
+
 ALL_PINS = [pin_bruteforce_rational, pin_integer_paths, pin_identities, pin_one_hot,
             pin_transpose, pin_closed_forms, pin_worked_example, pin_window, pin_fma_model,
-            pin_checksums, pin_empty]
+            pin_checksums, pin_empty, pin_transpose_golden, pin_transpose_closed_form,
+            pin_transpose_library_and_bits, pin_transpose_strides]
 
 
 def run_all(lib=None):

@@ -147,3 +147,22 @@ def test_bank_model_matches_page():
             assert models.conflict_degree(words, banks) == want, name
     # a 32-way conflict means 31 replays
     assert models.conflict_degree([r * 32 for r in range(32)], 32) - 1 == 31
+
+
+def test_transpose_models_match_page():
+    """The page's transpose kernels, thread by thread: both produce the
+    transpose (equal to the oracle's), and their per-warp DRAM bursts and
+    shared-memory conflicts are the page's (tests/golden/transpose_coalescing.txt)."""
+    M, N = 64, 96  # several tiles each way, not square
+    for parts in _lines("transpose_coalescing.txt"):
+        assert parts[0] == "kernel"
+        kind, pad, rd, wr, conflict = parts[1], int(parts[2]), int(parts[3]), int(parts[4]), int(parts[5])
+        run = models.transpose_run(M, N, kind, pad=pad)
+        A = np.array(run["A"], np.float32)
+        assert np.array_equal(np.array(run["B"], np.float32), oracle.transpose(A)), kind
+        assert {models.bursts(a) for a in run["reads"]} == {rd}, (kind, pad, "reads")
+        assert {models.bursts(a) for a in run["writes"]} == {wr}, (kind, pad, "writes")
+        worst = max((models.conflict_degree(w, 32) for w in run["lds_reads"]), default=0)
+        assert worst == conflict, (kind, pad, "shared-memory reads")
+        # every element read once and written once
+        assert sum(len(a) for a in run["reads"]) == M * N == sum(len(a) for a in run["writes"])

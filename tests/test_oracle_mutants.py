@@ -1,8 +1,9 @@
 """Plant one plausible mistake at a time in a copy of oracle.c (on the CPU)
 and check that at least one pin catches it.  This is how the pins show they
 are strong enough: a dropped term, a wrong sign, a transposed operand, a
-wrong index, a missing absolute value, an unfused step or a wrong checksum
-weight must each fail something."""
+wrong index, a missing absolute value, an unfused step, a wrong checksum
+weight, or a transpose that drops a column, ignores a leading dimension or
+mirrors its output must each fail something."""
 
 import os
 import shutil
@@ -28,6 +29,11 @@ MUTANTS = {
     "fma_unfused": ("acc = fmaf(A[i * lda + k], B[k * ldb + j], acc);",
                     "acc = A[i * lda + k] * B[k * ldb + j] + acc;"),
     "checksum_weight": ("r += a * bsum[k];", "r += a * babs[k];"),
+    "transpose_last_column_dropped": ("for (int64_t j = 0; j < N; ++j) B[j * ldb + i]",
+                                      "for (int64_t j = 0; j < N - (N > 1); ++j) B[j * ldb + i]"),
+    "transpose_ignores_lda": ("B[j * ldb + i] = A[i * lda + j];", "B[j * ldb + i] = A[i * N + j];"),
+    "transpose_ignores_ldb": ("B[j * ldb + i] = A[i * lda + j];", "B[j * M + i] = A[i * lda + j];"),
+    "transpose_mirrored": ("B[j * ldb + i] = A[i * lda + j];", "B[j * ldb + (M - 1 - i)] = A[i * lda + j];"),
     "first_row_skipped": ("for (int64_t i = i0; i < i1; ++i) {", "for (int64_t i = i0 + (i1 > i0 + 1); i < i1; ++i) {"),
 }
 

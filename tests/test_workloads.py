@@ -61,3 +61,17 @@ def test_sampled_blocks():
     assert blocks2 == blocks
     with pytest.raises(ValueError):
         wl.sample_blocks(wl.Workload("r", 100, 64, 8, "uniform", 0))
+
+
+def test_transpose_workloads():
+    ws = wl.TRANSPOSE_WORKLOADS
+    assert [(w.M, w.N) for w in ws.values()] == [(1024, 1024), (16384, 16384), (3001, 5003)]
+    assert ws["transpose16384_uniform"].algorithmic_bytes == 2 * 4 * 16384 ** 2
+    a = wl.random_matrix(300, 200, 10)
+    assert a.dtype == np.float32 and a.shape == (300, 200)
+    assert np.array_equal(a, wl.random_matrix(300, 200, 10))
+    assert not np.array_equal(a, wl.random_matrix(300, 200, 11))
+    assert a.min() >= -1.0 and a.max() < 1.0
+    # on the 2^-23 grid (2x - 1 of a float32 multiple of 2^-24 is exact)
+    assert np.array_equal(a * np.float32(2 ** 23), np.round(a * np.float32(2 ** 23)))
+    assert len(np.unique(a)) > 0.99 * a.size

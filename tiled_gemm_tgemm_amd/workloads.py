@@ -1,4 +1,4 @@
-"""Seeded synthetic input matrices for C = A·B.
+"""Seeded synthetic input matrices for C = A·B and for the transpose.
 
 This module draws numbers and nothing else: it holds none of the product's
 arithmetic, so both the HIP path (bench, parity tests) and the CPU oracle can
@@ -16,6 +16,13 @@ workload here is a synthetic stand-in of that shape family:
 * sampled output blocks (for the largest square case) are drawn from the same
   generator, continued after B, without replacement, on a grid aligned to the
   block size.
+
+The transpose of page 2 §1.4 is studied there on a 1024×1024 matrix; its
+workloads are that shape, one large enough that input and output (1 GiB
+each) stream from HBM rather than the last-level cache, and a ragged one.
+Their values are ``numpy.random.default_rng(seed).random(dtype=float32)``
+mapped to [-1, 1) (2x - 1, exact in float32): a transpose only moves words,
+so the value law matters only in that every word is distinct in practice.
 """
 
 from __future__ import annotations
@@ -111,3 +118,40 @@ def make_inputs_and_blocks(w: Workload, count: int = 64, size: int = 64):
     """(A, B, blocks) in one pass over the generator."""
     A, B, rng = random_matrices(w.M, w.N, w.K, w.dist, w.seed)
     return A, B, sample_blocks(w, count, size, rng)
+
+
+@dataclasses.dataclass(frozen=True)
+class TransposeWorkload:
+    name: str
+    M: int  # input rows (output columns)
+    N: int  # input columns (output rows)
+    seed: int
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Every element read once and written once: 2·4·M·N."""
+        return 8 * self.M * self.N
+
+
+TRANSPOSE_WORKLOADS = {
+    w.name: w
+    for w in (
+        TransposeWorkload("transpose1024_uniform", 1024, 1024, 10),
+        TransposeWorkload("transpose16384_uniform", 16384, 16384, 11),
+        # neither side a multiple of any tile; M·N about 15 M elements
+        TransposeWorkload("transpose3001x5003_uniform", 3001, 5003, 12),
+    )
+}
+
+
+def random_matrix(M: int, N: int, seed: int) -> np.ndarray:
+    """M×N float32, i.i.d. on the grid of multiples of 2^-23 in [-1, 1)."""
+    rng = np.random.default_rng(seed)
+    x = rng.random((M, N), dtype=np.float32)
+    x *= np.float32(2.0)
+    x -= np.float32(1.0)
+    return x
+
+
+def make_transpose_input(w: TransposeWorkload) -> np.ndarray:
+    return random_matrix(w.M, w.N, w.seed)
