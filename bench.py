@@ -9,6 +9,12 @@ and reported alongside, since the headline metric covers both sizes.
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
                   [--kernel auto|naive|lds16|lds32|simt|mfma:<variant>]
                   [--also NAME,...] [--no-cpu-baseline] [--copy-bytes N]
+  python bench.py --transpose blocked|naive|tiled|tiled_padded [--workload NAME]
+
+With --transpose the line measures B = Aᵀ (tgemm_transpose) instead, default
+workload 16384×16384: GB/s of algorithmic traffic (every element read once
+and written once) against the 8 TB/s HBM peak, a device-to-device copy of the
+same size timed beside it, and the oracle's transpose on the host.
 
 Warm-up: at least --warmup calls and at least --warmup-seconds of back-to-back
 calls (the GPU clock takes a few tens of milliseconds of load to settle).
@@ -79,6 +85,9 @@ def parse():
     p.add_argument("--cold", action="store_true",
                    help="before every timed call, overwrite a 512 MiB buffer so that L2 and the "
                         "256 MB Infinity Cache hold none of the operands (kernel time only)")
+    p.add_argument("--transpose", default=None,
+                   choices=("blocked", "naive", "tiled", "tiled_padded"),
+                   help="measure the transpose kernel instead of the product")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed steps, run one plain device-to-device copy of this many "
                         "bytes (a known-size reference for hardware byte counters)")
@@ -212,6 +221,107 @@ def cpu_baseline(m, target_s: float):
     }
 
 
+def time_transpose(w, kernel: str, steps: int, warmup: int, warmup_seconds: float):
+    """Time `steps` transposes of a resident input; also a plain copy of the same size."""
+    import numpy as np
+    import torch
+
+    import tiled_gemm_tgemm_amd as tg
+    from tiled_gemm_tgemm_amd import workloads as wl
+
+    A_h = wl.make_transpose_input(w)
+    A = torch.from_numpy(A_h).cuda()
+    B = torch.empty((w.N, w.M), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(call):
+        warm, t_warm = 0, time.perf_counter()
+        while warm < warmup or time.perf_counter() - t_warm < warmup_seconds:
+            call()
+            warm += 1
+            if warm % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            call()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        per = np.array([s_.elapsed_time(e) for s_, e in zip(starts, ends)])
+        return warm, wall_ms, per
+
+    warm, wall_ms, per = timed(lambda: tg.transpose(A, out=B, kernel=kernel))
+    copy_dst = torch.empty_like(A)
+    _, _, per_copy = timed(lambda: copy_dst.copy_(A))
+    del copy_dst
+    return {"workload": w, "A_host": A_h, "B": B, "warmup_launches": warm, "wall_ms": wall_ms,
+            "kernel_ms": float(per.mean()), "kernel_ms_min": float(per.min()),
+            "kernel_ms_median": float(np.median(per)), "kernel_ms_p90": float(np.percentile(per, 90)),
+            "copy_ms": float(per_copy.mean())}
+
+
+def transpose_main(args, props):
+    import numpy as np
+
+    from tiled_gemm_tgemm_amd import workloads as wl
+
+    name = args.workload if args.workload in wl.TRANSPOSE_WORKLOADS else "transpose16384_uniform"
+    w = wl.TRANSPOSE_WORKLOADS[name]
+    m = time_transpose(w, args.transpose, args.steps, args.warmup, args.warmup_seconds)
+    gbs = lambda ms: w.algorithmic_bytes / (ms * 1e-3) / 1e9  # noqa: E731
+    achieved = gbs(m["kernel_ms"])
+    line = {
+        "metric": "fp32 matrix transpose GB/s (bytes read + written) vs the 8 TB/s HBM peak",
+        "value": round(gbs(m["wall_ms"]), 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_launches": m["warmup_launches"],
+        "ms_per_step": round(m["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "seed": w.seed,
+                   "kernel": f"tgemm_transpose({args.transpose})"},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+        },
+        "kernel_ms": {"mean": round(m["kernel_ms"], 4), "min": round(m["kernel_ms_min"], 4),
+                      "median": round(m["kernel_ms_median"], 4), "p90": round(m["kernel_ms_p90"], 4)},
+        "copy_reference": {"what": "device-to-device copy of the same M·N floats",
+                           "gbs": round(gbs(m["copy_ms"]), 1), "ms": round(m["copy_ms"], 4),
+                           "transpose_over_copy": round(m["copy_ms"] / m["kernel_ms"], 4)},
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        A = m["A_host"]
+        reps, t = 0, 0.0
+        while t < args.cpu_seconds or reps == 0:
+            t0 = time.perf_counter()
+            Bo = oracle.transpose(A)
+            t += time.perf_counter() - t0
+            reps += 1
+        same = bool(np.array_equal(Bo.view(np.uint32), m["B"].cpu().numpy().view(np.uint32)))
+        line["cpu_baseline"] = {
+            "value": round(reps * w.algorithmic_bytes / t / 1e9, 2), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full transposes of {w.name} ({w.M}x{w.N}) by the oracle; {t:.2f} s",
+            "gpu_result_bit_exact": same,
+        }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -228,6 +338,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     props = torch.cuda.get_device_properties(0)
+    if args.transpose:
+        return transpose_main(args, props)
 
     w = wl.WORKLOADS[args.workload]
     m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,

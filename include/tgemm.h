@@ -184,6 +184,44 @@ tgemm_status_t tgemm_sgemm_simt(int64_t M, int64_t N, int64_t K,
                                 const float *B, int64_t ldb,
                                 float *C, int64_t ldc, hipStream_t stream);
 
+/* Kernels of tgemm_transpose. */
+typedef enum tgemm_transpose_kernel {
+    TGEMM_TRANSPOSE_BLOCKED = 0,     /* default: 4×4 blocks per thread, whole cache lines both ways */
+    TGEMM_TRANSPOSE_NAIVE = 1,       /* page 2 §1.4: rows in, strided stores out */
+    TGEMM_TRANSPOSE_TILED = 2,       /* page 2 §1.4: through a 32×32 LDS tile */
+    TGEMM_TRANSPOSE_TILED_PADDED = 3 /* page 2 §1.4: LDS tile with rows of 33 words */
+} tgemm_transpose_kernel_t;
+
+/*
+ * B = Aᵀ: the matrix transpose of page 2 ("Lec 29 · GPU Architecture (2)"),
+ * §1.4.  A is M×N row-major with leading dimension lda >= max(1, N); B is
+ * N×M row-major with ldb >= max(1, M); B(j, i) = A(i, j) for i < M, j < N,
+ * every element moved as a 32-bit word (bit patterns, NaN payloads and
+ * signed zeros arrive unchanged); nothing else of B is written.  Device
+ * pointers owned by the caller; B must not overlap A (no in-place
+ * transpose).  Asynchronous on `stream`.  M = 0 or N = 0 is a no-op.
+ *
+ * kernel selects the page's progression on this GPU — NAIVE (32×32 tiles,
+ * 32×8 threads, four elements per thread; reads along A's rows, stores down
+ * B's columns), TILED (the same tile staged through LDS, barrier, swapped
+ * block offsets, stores along B's rows), TILED_PADDED (LDS rows padded to 33
+ * words) — or BLOCKED, this library's kernel: no LDS; each thread moves
+ * 4×4 blocks, each with four 16-byte reads and four 16-byte writes, so a
+ * wavefront's every access is whole 128-byte runs (when A and B are 16-byte
+ * aligned and lda, ldb are multiples of 4; otherwise single-word accesses
+ * with the same mapping); from 2^24 elements on, four blocks side by side
+ * per thread.
+ *
+ * Errors: TGEMM_ERROR_INVALID_VALUE for negative sizes, short leading
+ * dimensions, null or misaligned pointers, or overlap;
+ * TGEMM_ERROR_NOT_SUPPORTED for an unknown kernel or a size above
+ * 2^31 - 2^16; TGEMM_ERROR_HIP if the launch fails.  Nothing is queued on
+ * an error.
+ */
+tgemm_status_t tgemm_transpose(int64_t M, int64_t N, const float *A, int64_t lda,
+                               float *B, int64_t ldb, tgemm_transpose_kernel_t kernel,
+                               hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *tgemm_status_string(tgemm_status_t status);
 

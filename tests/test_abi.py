@@ -56,7 +56,7 @@ def test_header_compiles_alone(tmp_path, compiler, std):
 
 
 def test_static_queries(lib):
-    assert tg.tgemm_version() == 100
+    assert tg.tgemm_version() == 200
     n = tg.tgemm_mfma_variant_count()
     assert n >= 6
     names = tg.variant_names()
@@ -203,3 +203,41 @@ def test_variant_choice(lib):
     assert chosen(64, 64, 64, a=(1 << 40) + 4).endswith("vec1")  # A not 16-byte aligned
     assert chosen(0, 4, 4) is None and chosen(4, 4, 0) is None
     assert tg.tgemm_sgemm_variant_for(4, 4, 4, A_, 2, B_, 4, C_, 4) == -1  # lda < K
+
+
+def test_header_enums_match_binding():
+    text = open(HEADER).read()
+    for name in ("TGEMM_OP_N", "TGEMM_OP_T", "TGEMM_TRANSPOSE_BLOCKED", "TGEMM_TRANSPOSE_NAIVE",
+                 "TGEMM_TRANSPOSE_TILED", "TGEMM_TRANSPOSE_TILED_PADDED", "TGEMM_SUCCESS",
+                 "TGEMM_ERROR_INVALID_VALUE", "TGEMM_ERROR_NOT_SUPPORTED", "TGEMM_ERROR_HIP"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(_lib, name), name
+
+
+TRANSPOSE_CASES = [
+    ((-1, 4, A_, 4, B_, 1), INVALID),
+    ((4, -1, A_, 1, B_, 4), INVALID),
+    ((4, 8, A_, 7, B_, 4), INVALID),                # lda < N
+    ((4, 8, A_, 8, B_, 3), INVALID),                # ldb < M
+    ((4, 8, 0, 8, B_, 4), INVALID),                 # null A
+    ((4, 8, A_, 8, 0, 4), INVALID),                 # null B
+    ((4, 8, A_ + 2, 8, B_, 4), INVALID),            # misaligned A
+    ((4, 8, A_, 8, B_ + 1, 4), INVALID),            # misaligned B
+    ((4, 8, A_, 8, A_ + 4 * 31, 4), INVALID),       # B starts on A's last element
+    ((4, 8, B_ - 4 * 31, 8, B_, 4), INVALID),       # A ends on B's first element
+    ((MAX_DIM + 1, 1, A_, 1, B_, MAX_DIM + 1), UNSUPPORTED),
+    ((4, 8, A_, 1 << 41, B_, 4), UNSUPPORTED),
+    ((0, 8, A_, 8, B_, 1), tg.TGEMM_SUCCESS),       # M = 0: nothing to do
+    ((4, 0, 0, 1, 0, 4), tg.TGEMM_SUCCESS),         # N = 0 ignores pointers
+]
+
+
+@pytest.mark.parametrize("args,status", TRANSPOSE_CASES)
+def test_transpose_argument_checks(lib, args, status):
+    for kernel in range(4):
+        assert tg.tgemm_transpose(*args, kernel, None) == status, kernel
+
+
+def test_transpose_kernel_choice_checks(lib):
+    for kernel in (-1, 4, 99):
+        assert tg.tgemm_transpose(4, 8, A_, 8, B_, 4, kernel, None) == UNSUPPORTED

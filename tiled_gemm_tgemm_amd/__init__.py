@@ -2,8 +2,8 @@
 
 The compute lives in the C-ABI library libtgemm.so (sources in csrc/,
 declarations in include/tgemm.h).  ``_lib`` exposes the C entry points under
-their own names; ``sgemm`` below is the same call for torch tensors, with
-torch used for device memory and the current stream only.
+their own names; ``sgemm`` and ``transpose`` below are the same calls for
+torch tensors, with torch used for device memory and the current stream only.
 
 Nothing here loads the library at import time; the first call does, and it
 raises if libtgemm.so has not been built (``python -m
@@ -19,6 +19,10 @@ from ._lib import (  # noqa: F401
     TGEMM_ERROR_INVALID_VALUE,
     TGEMM_ERROR_NOT_SUPPORTED,
     TGEMM_SUCCESS,
+    TGEMM_TRANSPOSE_BLOCKED,
+    TGEMM_TRANSPOSE_NAIVE,
+    TGEMM_TRANSPOSE_TILED,
+    TGEMM_TRANSPOSE_TILED_PADDED,
     TgemmError,
     library,
     tgemm_mfma_variant_count,
@@ -33,6 +37,7 @@ from ._lib import (  # noqa: F401
     tgemm_sgemm_simt,
     tgemm_sgemm_variant_for,
     tgemm_status_string,
+    tgemm_transpose,
     tgemm_version,
 )
 
@@ -110,6 +115,40 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
         raise ValueError(f"kernel must be one of {KERNELS}")
     if st != TGEMM_SUCCESS:
         raise TgemmError(st, f"tgemm ({kernel})")
+    return out
+
+
+TRANSPOSE_KERNELS = {"blocked": TGEMM_TRANSPOSE_BLOCKED, "naive": TGEMM_TRANSPOSE_NAIVE,
+                     "tiled": TGEMM_TRANSPOSE_TILED, "tiled_padded": TGEMM_TRANSPOSE_TILED_PADDED}
+
+
+def transpose(A, out=None, *, kernel="blocked", stream=None):
+    """B = Aᵀ (tgemm_transpose) for a row-major float32 CUDA tensor A (any row
+    stride); `out`, if given, must be row-major N×M and not overlap A.
+    kernel: "blocked" (default), "naive", "tiled" or "tiled_padded".  Queued
+    on `stream` (default: torch's current stream); returns `out` without waiting."""
+    import torch
+
+    A = _check(A, "A")
+    M, N = A.shape
+    if A.stride(1) != 1 and N > 1:
+        raise ValueError("A must be row-major")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float32, device=A.device)
+    else:
+        out = _check(out, "out")
+        if tuple(out.shape) != (N, M):
+            raise ValueError(f"out must be {N}x{M}")
+        if out.stride(1) != 1 and M > 1:
+            raise ValueError("out must be row-major")
+    if kernel not in TRANSPOSE_KERNELS:
+        raise ValueError(f"kernel must be one of {tuple(TRANSPOSE_KERNELS)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    st = tgemm_transpose(M, N, A.data_ptr(), max(A.stride(0), N, 1), out.data_ptr(), max(out.stride(0), M, 1),
+                         TRANSPOSE_KERNELS[kernel], stream)
+    if st != TGEMM_SUCCESS:
+        raise TgemmError(st, f"tgemm_transpose ({kernel})")
     return out
 
 

@@ -25,6 +25,11 @@ _ptr = ctypes.c_void_p
 _GEMM = [_i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64]
 TGEMM_OP_N = 0
 TGEMM_OP_T = 1
+# tgemm_transpose_kernel_t values
+TGEMM_TRANSPOSE_BLOCKED = 0
+TGEMM_TRANSPOSE_NAIVE = 1
+TGEMM_TRANSPOSE_TILED = 2
+TGEMM_TRANSPOSE_TILED_PADDED = 3
 
 SIGNATURES = {
     "tgemm_sgemm": (ctypes.c_int, _GEMM + [_ptr]),
@@ -38,6 +43,7 @@ SIGNATURES = {
     "tgemm_sgemm_naive": (ctypes.c_int, _GEMM + [_ptr]),
     "tgemm_sgemm_lds": (ctypes.c_int, _GEMM + [ctypes.c_int, ctypes.c_int, _ptr]),
     "tgemm_sgemm_simt": (ctypes.c_int, _GEMM + [_ptr]),
+    "tgemm_transpose": (ctypes.c_int, [_i64, _i64, _ptr, _i64, _ptr, _i64, ctypes.c_int, _ptr]),
     "tgemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tgemm_version": (ctypes.c_int, []),
 }
@@ -99,6 +105,10 @@ def tgemm_sgemm_lds(M, N, K, A, lda, B, ldb, C, ldc, tile, pad, stream=None) -> 
 
 def tgemm_sgemm_simt(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return library().tgemm_sgemm_simt(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tgemm_transpose(M, N, A, lda, B, ldb, kernel=TGEMM_TRANSPOSE_BLOCKED, stream=None) -> int:
+    return library().tgemm_transpose(M, N, A, lda, B, ldb, kernel, stream)
 
 
 def tgemm_mfma_variant_count() -> int:

@@ -252,6 +252,33 @@ tgemm_status_t tgemm_sgemm_simt(int64_t M, int64_t N, int64_t K, const float *A,
     return from_hip(tgemm::launch_simt_tiled(pack(false, false, M, N, K, A, lda, B, ldb, C, ldc), stream));
 }
 
+tgemm_status_t tgemm_transpose(int64_t M, int64_t N, const float *A, int64_t lda, float *B, int64_t ldb,
+                               tgemm_transpose_kernel_t kernel, hipStream_t stream)
+{
+    if (M < 0 || N < 0 || lda < max1(N) || ldb < max1(M)) return TGEMM_ERROR_INVALID_VALUE;
+    tgemm::TransposeKind kind;
+    switch (kernel) {
+        case TGEMM_TRANSPOSE_BLOCKED: kind = tgemm::TransposeKind::kBlocked; break;
+        case TGEMM_TRANSPOSE_NAIVE: kind = tgemm::TransposeKind::kNaive; break;
+        case TGEMM_TRANSPOSE_TILED: kind = tgemm::TransposeKind::kTiled; break;
+        case TGEMM_TRANSPOSE_TILED_PADDED: kind = tgemm::TransposeKind::kTiledPadded; break;
+        default: return TGEMM_ERROR_NOT_SUPPORTED;
+    }
+    if (M > kMaxDim || N > kMaxDim || lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40)
+        return TGEMM_ERROR_NOT_SUPPORTED;
+    if (M == 0 || N == 0) return TGEMM_SUCCESS;
+    if (A == nullptr || B == nullptr || reinterpret_cast<uintptr_t>(A) % alignof(float) ||
+        reinterpret_cast<uintptr_t>(B) % alignof(float))
+        return TGEMM_ERROR_INVALID_VALUE;
+    uintptr_t a0, a1, b0, b1;
+    span(A, M, N, lda, a0, a1);
+    span(B, N, M, ldb, b0, b1);
+    if (overlaps(a0, a1, b0, b1)) return TGEMM_ERROR_INVALID_VALUE;
+    const bool vec4 = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
+    return from_hip(tgemm::launch_transpose(kind, tgemm::TransposeArgs{(int)M, (int)N, A, lda, B, ldb, vec4},
+                                            stream));
+}
+
 const char *tgemm_status_string(tgemm_status_t status)
 {
     switch (status) {
@@ -263,6 +290,6 @@ const char *tgemm_status_string(tgemm_status_t status)
     return "unknown status";
 }
 
-int tgemm_version(void) { return 100; }
+int tgemm_version(void) { return 200; }
 
 }  // extern "C"

@@ -35,6 +35,21 @@ hipError_t launch_simt_tiled(const GemmArgs &g, hipStream_t stream);
 // C(i,j) = +0 for i < M, j < N (the empty sum, K = 0).
 hipError_t launch_fill_zero(int M, int N, float *C, int64_t ldc, hipStream_t stream);
 
+// B (N×M) = Aᵀ for A (M×N): B[j*ldb + i] = A[i*lda + j].  vec4: A and B
+// 16-byte aligned and lda, ldb multiples of 4 (16-byte accesses allowed).
+struct TransposeArgs {
+    int M, N;
+    const float *A;
+    int64_t lda;
+    float *B;
+    int64_t ldb;
+    bool vec4;
+};
+
+enum class TransposeKind { kBlocked, kNaive, kTiled, kTiledPadded };
+
+hipError_t launch_transpose(TransposeKind kind, const TransposeArgs &t, hipStream_t stream);
+
 // Matrix-core tile configurations.
 struct MfmaVariant {
     const char *name;
