@@ -10,11 +10,16 @@ and reported alongside, since the headline metric covers both sizes.
                   [--kernel auto|naive|lds16|lds32|simt|mfma:<variant>]
                   [--also NAME,...] [--no-cpu-baseline] [--copy-bytes N]
   python bench.py --transpose blocked|naive|tiled|tiled_padded [--workload NAME]
+  python bench.py --host [--workload NAME] [--panel-rows R]
 
 With --transpose the line measures B = Aᵀ (tgemm_transpose) instead, default
 workload 16384×16384: GB/s of algorithmic traffic (every element read once
 and written once) against the 8 TB/s HBM peak, a device-to-device copy of the
 same size timed beside it, and the oracle's transpose on the host.
+
+With --host the line measures the product of operands in pinned HOST memory
+(tgemm_sgemm_host: transfers overlapped with the computation), host to host,
+against the same steps run one after the other on one stream.
 
 Warm-up: at least --warmup calls and at least --warmup-seconds of back-to-back
 calls (the GPU clock takes a few tens of milliseconds of load to settle).
@@ -88,6 +93,9 @@ def parse():
     p.add_argument("--transpose", default=None,
                    choices=("blocked", "naive", "tiled", "tiled_padded"),
                    help="measure the transpose kernel instead of the product")
+    p.add_argument("--host", action="store_true",
+                   help="measure tgemm_sgemm_host (host operands, copies overlapped with the product)")
+    p.add_argument("--panel-rows", type=int, default=0, help="panel height for --host (0: the library's)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed steps, run one plain device-to-device copy of this many "
                         "bytes (a known-size reference for hardware byte counters)")
@@ -322,6 +330,99 @@ def transpose_main(args, props):
     return 0
 
 
+def host_main(args, props):
+    """Host-to-host product with overlapped transfers vs the same steps in series."""
+    import numpy as np
+    import torch
+
+    import tiled_gemm_tgemm_amd as tg
+    from tiled_gemm_tgemm_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    A_h, B_h = wl.make_inputs(w)
+    A = torch.from_numpy(A_h).pin_memory()
+    B = torch.from_numpy(B_h).pin_memory()
+    C = torch.empty((w.M, w.N), dtype=torch.float32).pin_memory()
+    need = tg.tgemm_sgemm_host_workspace_size(w.M, w.N, w.K, args.panel_rows)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    streams = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+    dA = torch.empty((w.M, w.K), device="cuda")
+    dB = torch.empty((w.K, w.N), device="cuda")
+    dC = torch.empty((w.M, w.N), device="cuda")
+    torch.cuda.synchronize()
+
+    def overlapped():
+        tg.sgemm_host(A, B, out=C, panel_rows=args.panel_rows, streams=streams, workspace=ws)
+
+    def serial():
+        dA.copy_(A, non_blocking=True)
+        dB.copy_(B, non_blocking=True)
+        tg.sgemm(dA, dB, out=dC)
+        C.copy_(dC, non_blocking=True)
+        torch.cuda.synchronize()
+
+    def h2d():
+        dA.copy_(A, non_blocking=True)
+        torch.cuda.synchronize()
+
+    def d2h():
+        C.copy_(dC, non_blocking=True)
+        torch.cuda.synchronize()
+
+    def timed(fn):
+        warm, t_warm = 0, time.perf_counter()
+        while warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds:
+            fn()
+            warm += 1
+        ts = []
+        for _ in range(args.steps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.mean(ts)), float(np.min(ts))
+
+    t_ov, t_ov_min = timed(overlapped)
+    t_se, _ = timed(serial)
+    serial_c = C.numpy().copy()
+    overlapped()
+    same = bool(np.array_equal(C.numpy(), serial_c))
+    t_h2d, _ = timed(h2d)
+    t_d2h, _ = timed(d2h)
+    h2d_gbs = 4 * w.M * w.K / t_h2d / 1e9
+    d2h_gbs = 4 * w.M * w.N / t_d2h / 1e9
+    in_bytes, out_bytes = 4 * (w.M * w.K + w.K * w.N), 4 * w.M * w.N
+    tflops = w.flops / t_ov / 1e12
+    line = {
+        "metric": "host-to-host fp32 GEMM TFLOP/s, PCIe transfers included (overlapped with the product)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_ov * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
+                   "kernel": "tgemm_sgemm_host", "panel_rows": args.panel_rows or "library default",
+                   "host_memory": "pinned"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_MATRIX_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_MATRIX_TFLOPS, 4), "traffic": None},
+        "overlap": {
+            "overlapped_ms": round(t_ov * 1e3, 3), "overlapped_min_ms": round(t_ov_min * 1e3, 3),
+            "serial_ms": round(t_se * 1e3, 3), "speedup": round(t_se / t_ov, 3),
+            "h2d_gbs": round(h2d_gbs, 1), "d2h_gbs": round(d2h_gbs, 1),
+            "transfer_floor_ms": round(max(in_bytes / (h2d_gbs * 1e9), out_bytes / (d2h_gbs * 1e9)) * 1e3, 3),
+            "results_equal_serial": same,
+        },
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -340,6 +441,8 @@ def main():
     props = torch.cuda.get_device_properties(0)
     if args.transpose:
         return transpose_main(args, props)
+    if args.host:
+        return host_main(args, props)
 
     w = wl.WORKLOADS[args.workload]
     m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,

@@ -222,6 +222,45 @@ tgemm_status_t tgemm_transpose(int64_t M, int64_t N, const float *A, int64_t lda
                                float *B, int64_t ldb, tgemm_transpose_kernel_t kernel,
                                hipStream_t stream);
 
+/*
+ * C = A·B with A, B and C in HOST memory, the transfers overlapped with the
+ * product (page 1, section [CUDA Performance Considerations], "Overlap I/O
+ * with Computation": host↔device copies and computation at the same time,
+ * on streams).  B is copied to the device once; A and C move in panels of
+ * panel_rows rows (0: about M/4, rounded up to 256): while panel p is
+ * multiplied on `compute` (an ordinary tgemm_sgemm call), panel p+1 of A is
+ * copied in on `copy_in` and panel p-1 of C is copied out on `copy_out`.
+ * Pass three different streams for the copies to overlap (one stream, or
+ * NULL for all three, is correct but serial).  A, B, C should be page-locked
+ * (hipHostMalloc, or a pinned torch CPU tensor) for the copies to run
+ * asynchronously; pageable memory works but serialises them.
+ *
+ * Layout and semantics as tgemm_sgemm (row-major, leading dimensions in
+ * elements, C overwritten; K = 0 sets C to +0.0 on the host without device
+ * work; M = 0 or N = 0 is a no-op).  `workspace` is caller-owned DEVICE
+ * memory, 256-byte aligned, of at least tgemm_sgemm_host_workspace_size(M,
+ * N, K, panel_rows) bytes (B, two A panels and two C panels); the library
+ * allocates nothing.  Unlike the device entry points this call BLOCKS: it
+ * returns once C is complete in host memory (or after an error, once
+ * everything it queued has finished).
+ *
+ * Errors: TGEMM_ERROR_INVALID_VALUE for the device entry points' argument
+ * errors (host C overlapping host A or B), a negative panel_rows, or a
+ * missing, misaligned or too small workspace; TGEMM_ERROR_NOT_SUPPORTED for
+ * sizes as above; TGEMM_ERROR_HIP if a copy, event or launch fails (C may
+ * then be partly written).
+ */
+tgemm_status_t tgemm_sgemm_host(int64_t M, int64_t N, int64_t K,
+                                const float *A, int64_t lda,
+                                const float *B, int64_t ldb,
+                                float *C, int64_t ldc,
+                                void *workspace, int64_t workspace_bytes, int64_t panel_rows,
+                                hipStream_t compute, hipStream_t copy_in, hipStream_t copy_out);
+
+/* Device workspace bytes tgemm_sgemm_host needs; 0 if it needs none (M, N or
+ * K zero); -1 for invalid sizes or a negative panel_rows. */
+int64_t tgemm_sgemm_host_workspace_size(int64_t M, int64_t N, int64_t K, int64_t panel_rows);
+
 /* Static, human-readable text for a status code. */
 const char *tgemm_status_string(tgemm_status_t status);
 

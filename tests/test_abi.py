@@ -241,3 +241,47 @@ def test_transpose_argument_checks(lib, args, status):
 def test_transpose_kernel_choice_checks(lib):
     for kernel in (-1, 4, 99):
         assert tg.tgemm_transpose(4, 8, A_, 8, B_, 4, kernel, None) == UNSUPPORTED
+
+
+def test_host_workspace_size(lib):
+    MiB = 1 << 20
+    # B, then two A panels and two C panels of (about M/4 rounded up to 256) rows
+    assert tg.tgemm_sgemm_host_workspace_size(8192, 8192, 8192, 0) == 256 * MiB + 2 * 64 * MiB + 2 * 64 * MiB
+    assert tg.tgemm_sgemm_host_workspace_size(8192, 8192, 8192, 1024) == 256 * MiB + 4 * 32 * MiB
+    r = 256  # M = 300: about 75 rows, rounded up to one 256-row tile
+    assert tg.tgemm_sgemm_host_workspace_size(300, 10, 7, 0) == 512 + 2 * (r * 7 * 4) + 2 * (r * 10 * 4)
+    assert tg.tgemm_sgemm_host_workspace_size(100, 10, 7, 0) == 512 + 2 * 2816 + 2 * 4096  # panel = M
+    assert tg.tgemm_sgemm_host_workspace_size(0, 10, 7, 0) == 0
+    assert tg.tgemm_sgemm_host_workspace_size(10, 10, 0, 0) == 0
+    assert tg.tgemm_sgemm_host_workspace_size(-1, 10, 7, 0) == -1
+    assert tg.tgemm_sgemm_host_workspace_size(10, 10, 7, -5) == -1
+    assert tg.tgemm_sgemm_host_workspace_size(MAX_DIM + 1, 10, 7, 0) == -1
+
+
+W_ = 0x40000000  # fake 256-byte-aligned device workspace
+HOST_CASES = [
+    ((4, 4, 4, A_, 4, B_, 4, C_, 4, W_, 1 << 20, -1), INVALID),       # negative panel_rows
+    ((4, 4, 4, A_, 3, B_, 4, C_, 4, W_, 1 << 20, 0), INVALID),        # lda < K
+    ((4, 4, 4, A_, 4, B_, 4, C_, 4, 0, 1 << 20, 0), INVALID),         # no workspace
+    ((4, 4, 4, A_, 4, B_, 4, C_, 4, W_ + 16, 1 << 20, 0), INVALID),   # misaligned workspace
+    ((4, 4, 4, A_, 4, B_, 4, C_, 4, W_, 64, 0), INVALID),             # workspace too small
+    ((4, 4, 4, 0, 4, B_, 4, C_, 4, W_, 1 << 20, 0), INVALID),         # null A
+    ((4, 4, 4, A_, 4, B_, 4, A_ + 8, 4, W_, 1 << 20, 0), INVALID),    # C overlaps A
+    ((MAX_DIM + 1, 4, 4, A_, 4, B_, 4, C_, 4, W_, 1 << 20, 0), UNSUPPORTED),
+    ((0, 4, 4, A_, 4, B_, 4, C_, 4, 0, 0, 0), tg.TGEMM_SUCCESS),      # M = 0: nothing to do
+]
+
+
+@pytest.mark.parametrize("args,status", HOST_CASES)
+def test_host_argument_checks(lib, args, status):
+    assert tg.tgemm_sgemm_host(*args, None, None, None) == status
+
+
+def test_host_empty_sum_is_written_on_the_host(lib):
+    """K = 0 needs no device at all: C (with a leading dimension) becomes +0."""
+    import numpy as np
+
+    C = np.full((3, 7), np.nan, np.float32)
+    st = tg.tgemm_sgemm_host(3, 5, 0, 0, 1, 0, 5, C.ctypes.data, 7, 0, 0, 0, None, None, None)
+    assert st == tg.TGEMM_SUCCESS
+    assert np.all(C[:, :5] == 0) and not np.any(np.signbit(C[:, :5])) and np.all(np.isnan(C[:, 5:]))

@@ -35,6 +35,8 @@ from ._lib import (  # noqa: F401
     tgemm_sgemm_variant_for_ex,
     tgemm_sgemm_naive,
     tgemm_sgemm_simt,
+    tgemm_sgemm_host,
+    tgemm_sgemm_host_workspace_size,
     tgemm_sgemm_variant_for,
     tgemm_status_string,
     tgemm_transpose,
@@ -149,6 +151,48 @@ def transpose(A, out=None, *, kernel="blocked", stream=None):
                          TRANSPOSE_KERNELS[kernel], stream)
     if st != TGEMM_SUCCESS:
         raise TgemmError(st, f"tgemm_transpose ({kernel})")
+    return out
+
+
+def sgemm_host(A, B, out=None, *, panel_rows=0, streams=None, workspace=None):
+    """C = A·B for float32 CPU tensors (tgemm_sgemm_host): copies overlapped
+    with the product, C returned in host memory.  A, B (and `out`) should be
+    pinned (``pin_memory()``) for the copies to overlap; rows may have any
+    stride.  streams: (compute, copy_in, copy_out) torch streams, default
+    three new ones on the current device; workspace: a CUDA uint8 tensor of
+    at least tgemm_sgemm_host_workspace_size bytes (allocated if omitted).
+    Blocks until C is complete."""
+    import torch
+
+    for t, name in ((A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2 or t.is_cuda:
+            raise TypeError(f"{name} must be a 2-D float32 CPU tensor")
+        if t.stride(1) != 1 and t.shape[1] > 1 and t.numel() > 0:
+            raise ValueError(f"{name} must be row-major")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, pin_memory=A.is_pinned())
+    elif out.is_cuda or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1 and out.numel() > 0):
+        raise ValueError(f"out must be a row-major {M}x{N} CPU tensor")
+    need = tgemm_sgemm_host_workspace_size(M, N, K, panel_rows)
+    if need < 0:
+        raise ValueError("invalid sizes or panel_rows")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    if streams is None:
+        streams = (torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream())
+    # the streams start after work already queued on the current stream (e.g. the
+    # workspace allocation)
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    st = tgemm_sgemm_host(M, N, K, A.data_ptr(), max(A.stride(0), K, 1), B.data_ptr(), max(B.stride(0), N, 1),
+                          out.data_ptr(), max(out.stride(0), N, 1), workspace.data_ptr(), workspace.numel(),
+                          panel_rows, *(s.cuda_stream for s in streams))
+    if st != TGEMM_SUCCESS:
+        raise TgemmError(st, "tgemm_sgemm_host")
     return out
 
 

@@ -44,6 +44,8 @@ SIGNATURES = {
     "tgemm_sgemm_lds": (ctypes.c_int, _GEMM + [ctypes.c_int, ctypes.c_int, _ptr]),
     "tgemm_sgemm_simt": (ctypes.c_int, _GEMM + [_ptr]),
     "tgemm_transpose": (ctypes.c_int, [_i64, _i64, _ptr, _i64, _ptr, _i64, ctypes.c_int, _ptr]),
+    "tgemm_sgemm_host": (ctypes.c_int, _GEMM + [_ptr, _i64, _i64, _ptr, _ptr, _ptr]),
+    "tgemm_sgemm_host_workspace_size": (_i64, [_i64, _i64, _i64, _i64]),
     "tgemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tgemm_version": (ctypes.c_int, []),
 }
@@ -109,6 +111,16 @@ def tgemm_sgemm_simt(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def tgemm_transpose(M, N, A, lda, B, ldb, kernel=TGEMM_TRANSPOSE_BLOCKED, stream=None) -> int:
     return library().tgemm_transpose(M, N, A, lda, B, ldb, kernel, stream)
+
+
+def tgemm_sgemm_host(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, panel_rows,
+                     compute=None, copy_in=None, copy_out=None) -> int:
+    return library().tgemm_sgemm_host(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                                      panel_rows, compute, copy_in, copy_out)
+
+
+def tgemm_sgemm_host_workspace_size(M, N, K, panel_rows=0) -> int:
+    return library().tgemm_sgemm_host_workspace_size(M, N, K, panel_rows)
 
 
 def tgemm_mfma_variant_count() -> int:
