@@ -55,9 +55,10 @@ PEAK_HBM_GBS = 8000.0
 # 16 lanes × 2 flops per FMA × 2.4 GHz
 PEAK_FP32_VECTOR_FMA_TFLOPS = 78.6
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/mfma_common.h",
-                  "tiled_gemm_tgemm_amd/csrc/mfma_sgemm_small.hip",
-                  "tiled_gemm_tgemm_amd/csrc/api.cpp", "tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h"]
+TRANSPOSE_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "transpose_traffic.json")
+TRANSPOSE_SOURCE = "tiled_gemm_tgemm_amd/csrc/transpose.hip"
+# the sources of the product kernel whose counters profiles/traffic.json holds
+KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/mfma_common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -185,18 +186,32 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
     }
 
 
-def traffic_for(workload_name: str, kernel_desc: str):
+def traffic_for(workload_name: str, variant: str):
     """Measured HBM bytes per launch from the committed counter summary, or None."""
     if not os.path.exists(TRAFFIC_RECORD):
         return None
     with open(TRAFFIC_RECORD) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
-        return None  # the kernel changed since the counters were taken
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("kernel") != variant:
+        return None  # the kernel changed since the counters were taken, or another one runs
     entry = rec.get("workloads", {}).get(workload_name)
     if not entry:
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def transpose_traffic_for(workload_name: str, kernel: str):
+    """Measured bytes per launch of a transpose kernel from the committed record, or None."""
+    if not os.path.exists(TRANSPOSE_TRAFFIC_RECORD):
+        return None
+    with open(TRANSPOSE_TRAFFIC_RECORD) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, TRANSPOSE_SOURCE), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest or rec.get("kernel") != kernel:
+        return None
+    entry = rec.get("workloads", {}).get(workload_name)
+    return entry.get("hbm_bytes_per_launch") if entry else None
 
 
 def cpu_baseline(m, target_s: float):
@@ -300,7 +315,8 @@ def transpose_main(args, props):
                    "kernel": f"tgemm_transpose({args.transpose})"},
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": transpose_traffic_for(w.name, args.transpose),
         },
         "kernel_ms": {"mean": round(m["kernel_ms"], 4), "min": round(m["kernel_ms_min"], 4),
                       "median": round(m["kernel_ms_median"], 4), "p90": round(m["kernel_ms_p90"], 4)},
@@ -427,7 +443,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs "
-              "are outside this build.", file=sys.stderr)
+              "are not supported.", file=sys.stderr)
         return 2
     import torch
 
@@ -448,7 +464,7 @@ def main():
     m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,
                       args.op_a, args.op_b)
     plain = args.kernel == "auto" and args.op_a == "N" and args.op_b == "N" and not args.cold
-    traffic = traffic_for(w.name, m["desc"]) if plain else None
+    traffic = traffic_for(w.name, m["variant"]) if plain else None
     achieved = m["tflops_kernel"]
     # kernels that multiply on the vector ALUs are held to the fma rate
     on_valu = args.kernel in ("naive", "simt") or args.kernel.startswith("lds")
