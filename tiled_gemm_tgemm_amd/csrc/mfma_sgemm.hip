@@ -20,19 +20,27 @@
 //   need no per-element tests and no load leaves the operand.  Only the last,
 //   partial phase of K masks A's columns explicitly; B's rows past K fall
 //   outside its extent on their own.
-// * LDS holds two stages.  Phase p computes from stage p%2; then the loads
-//   for phase p+1 are issued and written to the other stage.  One barrier per
-//   phase covers both of the pages' reasons to synchronise (page 1,
-//   "__syncthreads( )"): the stage about to be read is complete, and the
-//   stage about to be refilled was last read before the previous barrier.
-//   The loads go out after the phase's matrix-core work, not before it, and
-//   a wavefront raises its issue priority for the matrix-core block: with two
-//   work-groups per compute unit the two wavefronts of a SIMD then take
-//   turns, one multiplying while the other loads, stores and waits at its
-//   barrier.  Measured on MI355X at 8192³: loads first 88.5% of peak, loads
-//   after 90.4%, loads after with the priority raise 91.6%.  The main loop
-//   has no branches (the partial K phase is peeled off after it) and is not
-//   unrolled.
+// * LDS holds two stages and registers hold two more phases in flight.
+//   Phase p computes from stage p%2; then phase p+1, whose loads were issued
+//   two phases earlier, is written from registers to the other stage, the
+//   loads of phase p+3 are issued into the registers just freed, and one
+//   barrier ends the phase.  That barrier covers both of the pages' reasons
+//   to synchronise (page 1, "__syncthreads( )"): the stage about to be read
+//   is complete, and the stage about to be refilled was last read before the
+//   previous barrier.  A load thus has two phases of matrix-core work (its
+//   own wavefront's and, with two work-groups per compute unit, the other
+//   wavefront's on the same SIMD) to arrive, so a miss in L2 rarely stalls
+//   the LDS write.  The two register sets alternate, so the main loop is
+//   unrolled by two and has no branches; the last phases (the partial K
+//   phase among them) run in a tail loop.  Measured on MI355X at 8192³
+//   (4096³), bit-identical results, by how many phases ahead of its
+//   computation a phase's loads are issued: one (the next phase only, issued
+//   after the matrix-core block with its issue priority raised) 92.4%
+//   (91.0%) of peak; two (one register set) 93.5% (92.3%); three (this
+//   schedule) 94.7% (93.4%); four needs a third register set, which spills
+//   at this tile and is no better at the smaller ones.  With loads in flight
+//   across phases, raising the priority of the matrix-core block costs 4-5
+//   points, so it is not raised.
 // * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
@@ -166,6 +174,7 @@ struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, VEC = VEC_;
     static constexpr int GROUP_M = GROUP_M_;
     static constexpr int OCC = OCC_;                   // wavefronts per SIMD to budget registers for
+    static constexpr int NS = 2;                       // register sets of staged loads (see the kernel)
     static constexpr bool TA = TA_, TB = TB_;          // operands stored transposed
     static constexpr int NT = kWave * WM * WN;         // threads per work-group
     static constexpr int TM = BM / WM, TN = BN / WN;   // wavefront sub-tile
@@ -203,22 +212,19 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
     const int wm = wave / G::WN, wn = wave % G::WN;
     const int l32 = lane % 32, half = lane / 32;
 
-    LA la;
-    LB lb;
-    la.init(t, lda, rows_valid);
-    lb.init(t, ldb, cols_valid);
+    // NS register sets of staged loads: phase r travels in set (r - 1) mod NS
+    LA la[G::NS];
+    LB lb[G::NS];
+    la[0].init(t, lda, rows_valid);
+    lb[0].init(t, ldb, cols_valid);
+#pragma unroll
+    for (int s = 1; s < G::NS; ++s) {
+        la[s] = la[0];
+        lb[s] = lb[0];
+    }
     // operand pointers at (m0, 0) and (n0, 0) in their own storage order
     const float *a_tile = A + (LA::KC ? (int64_t)m0 * lda : (int64_t)m0);
     const float *b_tile = B + (LB::KC ? (int64_t)n0 * ldb : (int64_t)n0);
-    auto load_phase = [&] __device__(int k0, bool partial) {
-        la.issue(a_tile, lda, k0, K, rows_valid, partial);
-        lb.issue(b_tile, ldb, k0, K, cols_valid, partial);
-    };
-    auto store_phase = [&] __device__(int stage) {
-        float *s = lds + stage * G::STAGE;
-        la.store(s);
-        lb.store(s + G::A_STAGE);
-    };
 
     f32x16 acc[G::FM][G::FN];
 #pragma unroll
@@ -242,29 +248,51 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
                                                                                a_frag, b_frag);
     };
 
-    const int full = K / G::BK;            // phases with all BK values of k
-    const bool partial = K % G::BK != 0;   // one more, shorter phase
-    load_phase(0, full == 0);
-    store_phase(0);
+    const int full = K / G::BK;                  // phases with all BK values of k
+    const int nphase = full + (K % G::BK != 0);  // plus a shorter last one
+    // set s: issue the loads of phase r (the partial one if r == full) / write it to LDS stage r % 2
+    auto issue = [&] __device__(int s, int r, bool last) {
+        la[s].issue(a_tile, lda, r * G::BK, K, rows_valid, last);
+        lb[s].issue(b_tile, ldb, r * G::BK, K, cols_valid, last);
+    };
+    auto store = [&] __device__(int s, int r) {
+        float *st = lds + (r & 1) * G::STAGE;
+        la[s].store(st);
+        lb[s].store(st + G::A_STAGE);
+    };
+
+    issue(G::NS - 1, 0, full == 0);
+    store(G::NS - 1, 0);
+#pragma unroll
+    for (int s = 0; s < G::NS; ++s)
+        if (s + 1 < nphase) issue(s, s + 1, s + 1 == full);
     __syncthreads();
     int p = 0;
 #pragma unroll 1
-    for (; p + 1 < full; ++p) {            // the next phase is a full one
-        __builtin_amdgcn_s_setprio(1);     // the SIMD's other wavefront is loading: compute first
-        compute(p & 1);
-        __builtin_amdgcn_s_setprio(0);
-        load_phase((p + 1) * G::BK, false);
-        store_phase((p + 1) & 1);
-        __syncthreads();
+    for (; p + 2 * G::NS < full; p += G::NS) {  // every phase loaded in here is a full one
+#pragma unroll
+        for (int s = 0; s < G::NS; ++s) {
+            compute((p + s) & 1);
+            store(s, p + s + 1);
+            issue(s, p + s + 1 + G::NS, false);
+            __syncthreads();
+        }
     }
-    if (partial && full > 0) {
-        compute(p & 1);
-        load_phase(full * G::BK, true);
-        store_phase((p + 1) & 1);
-        __syncthreads();
-        ++p;
+#pragma unroll 1
+    for (; p < nphase; p += G::NS) {
+#pragma unroll
+        for (int s = 0; s < G::NS; ++s) {
+            const int r = p + s;
+            if (r < nphase) {
+                compute(r & 1);
+                if (r + 1 < nphase) {
+                    store(s, r + 1);
+                    if (r + 1 + G::NS < nphase) issue(s, r + 1 + G::NS, r + 1 + G::NS == full);
+                    __syncthreads();
+                }
+            }
+        }
     }
-    compute(p & 1);
 
     mfma::store_c<G::FM, G::FN>(acc, C, ldc, M, N, m0 + wm * G::TM, n0 + wn * G::TN, half, l32);
 }
@@ -333,14 +361,15 @@ typedef Shape<64, 64, 32, 1, 8, 4> Small1;
             max_ld<typename S::template C<false, true>::LB>(), true, alone, full, 7000.0, &S::launch \
     }
 
-// Efficiencies measured on MI355X (square and ragged shapes from 512 to 8192).
+// Efficiencies measured on MI355X: 256 tiles with K = 8192 (one work-group per
+// CU) and four full rounds with K = 4096, as fractions of the matrix-core peak.
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.70, 0.91),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.68, 0.88),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.49, 0.77),
-    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.66, 0.86),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.64, 0.84),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.47, 0.74),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.86, 0.94),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.83, 0.90),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.70, 0.86),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.81, 0.93),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.78, 0.90),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.63, 0.85),
 };
 
 }  // namespace
