@@ -291,6 +291,25 @@ def test_partial_phases_integer_exact(K):
     assert_exact(run(A, B), Pi, "auto")
 
 
+RING_KS = sorted({16 * f + r for f in range(4, 13) for r in (0, 5)} |
+                 {32 * f + r for f in range(4, 10) for r in (0, 9)})
+
+
+@pytest.mark.parametrize("K", RING_KS)
+def test_phase_ring_tail_integer_exact(K):
+    """The tiled kernels run their main loop two phases at a time and finish
+    in a tail loop; K sweeps the number of full phases (4 to 12 at depth 16,
+    4 to 9 at depth 32), with and without a shorter last phase, so the main
+    loop hands over to the tail at every offset.  Integers, exact."""
+    M, N = 259, 131 if K % 4 else 132
+    A, B = int_inputs(M, N, K, 2000 + K)
+    Pi = oracle.gemm_i64(A, B)
+    log(f"phase ring K={K}")
+    for v, name in enumerate(variants()):
+        if runnable(name, M, N, K):
+            assert_exact(run(A, B, "mfma", variant=v), Pi, f"{name} K={K}")
+
+
 def test_leading_dimension_beyond_buffer_offsets():
     """lda past what 32-bit buffer offsets cover: tgemm_sgemm runs the 64-bit
     pointer configuration, buffer configurations refuse it."""
