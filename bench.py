@@ -33,7 +33,10 @@ Reported:
   measured HBM traffic per launch comes from the committed rocprofv3 counter
   summary when it was taken on the current kernel source, else null;
 * cpu_baseline — the CPU oracle (float64, test infrastructure) timed on this
-  host's cores on a bounded sample: whole rows of the same product.
+  host's cores on a bounded sample: whole rows of the same product;
+* vendor_blas — context only: torch.matmul in float32 with TF32 off (the ROCm
+  BLAS library behind it) timed the same way on the same resident operands,
+  with the largest difference from this library's output (--no-vendor skips it).
 """
 
 from __future__ import annotations
@@ -82,6 +85,8 @@ def parse():
     p.add_argument("--also", default="square4096_uniform",
                    help="comma-separated extra workloads timed the same way ('' for none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-vendor", action="store_true",
+                   help="skip timing the vendor BLAS (torch.matmul, fp32) beside the product")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--op-a", choices=("N", "T"), default="N",
@@ -176,7 +181,7 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
     wall_ms = float(per.mean()) if cold else (t1 - t0) * 1e3 / steps
     kernel_ms = float(per.mean())
     return {
-        "workload": w, "A_host": A_h, "B_host": B_h, "C": C, "desc": desc, "variant": variant,
+        "workload": w, "A_host": A_h, "B_host": B_h, "A": A, "B": B, "C": C, "desc": desc, "variant": variant,
         "warmup_launches": warm,
         "wall_ms": wall_ms, "kernel_ms": kernel_ms,
         "kernel_ms_min": float(per.min()), "kernel_ms_median": float(np.median(per)),
@@ -184,6 +189,40 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
         "tflops_wall": w.flops / (wall_ms * 1e-3) / 1e12,
         "tflops_kernel": w.flops / (kernel_ms * 1e-3) / 1e12,
     }
+
+
+def vendor_blas(m, steps: int, warmup_seconds: float):
+    """torch.matmul (fp32, TF32 off) on the same resident operands, timed like the product."""
+    import numpy as np
+    import torch
+
+    torch.backends.cuda.matmul.allow_tf32 = False
+    w, A, B = m["workload"], m["A"], m["B"]
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    t_warm = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t_warm < warmup_seconds:
+        torch.matmul(A, B, out=C)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        torch.matmul(A, B, out=C)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    diff = float((C - m["C"]).abs().max().item())
+    return {"what": "torch.matmul float32, TF32 off (ROCm BLAS); context, not a target",
+            "kernel_ms_mean": round(ms, 4), "tflops": round(tflops, 3),
+            "pct_of_fp32_matrix_peak": round(100.0 * tflops / PEAK_FP32_MATRIX_TFLOPS, 2),
+            "tgemm_over_vendor": round(m["tflops_kernel"] / tflops, 4),
+            "max_abs_diff_vs_tgemm": diff}
 
 
 def traffic_for(workload_name: str, variant: str):
@@ -498,6 +537,10 @@ def main():
         "algorithmic_hbm_gbs": round(w.algorithmic_bytes / (m["kernel_ms"] * 1e-3) / 1e9, 1),
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
     }
+    # the vendor library computes the plain product; compare only what it computes
+    vendor = not args.no_vendor and args.kernel == "auto" and not args.cold
+    if vendor:
+        line["vendor_blas"] = vendor_blas(m, args.steps, args.warmup_seconds)
     also = {}
     for name in [x for x in args.also.split(",") if x and x != w.name]:
         wa = wl.WORKLOADS[name]
@@ -512,6 +555,8 @@ def main():
             "algorithmic_hbm_gbs": round(wa.algorithmic_bytes / (ma["kernel_ms"] * 1e-3) / 1e9, 1),
             "variant": ma["variant"],
         }
+        if vendor:
+            also[name]["vendor_blas"] = vendor_blas(ma, args.steps, args.warmup_seconds)
         del ma
     if also:
         line["also"] = also
