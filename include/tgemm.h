@@ -61,7 +61,8 @@ typedef enum tgemm_op {
 
 typedef enum tgemm_status {
     TGEMM_SUCCESS = 0,
-    TGEMM_ERROR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer or overlap */
+    TGEMM_ERROR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer or overlap, or an
+                                      operand that would run past the end of the address space */
     TGEMM_ERROR_NOT_SUPPORTED = 2, /* a size above 2^31-2^16, or an unknown kernel choice */
     TGEMM_ERROR_HIP = 3            /* the HIP runtime refused the launch */
 } tgemm_status_t;

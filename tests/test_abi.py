@@ -105,6 +105,11 @@ CASES = [
     ((0, 4, 4, A_, 4, B_, 4, C_, 4), tg.TGEMM_SUCCESS),  # M = 0: nothing to do
     ((4, 0, 4, A_, 4, B_, 1, C_, 1), tg.TGEMM_SUCCESS),  # N = 0
     ((0, 4, 4, 0, 4, 0, 4, 0, 4), tg.TGEMM_SUCCESS),     # no-op ignores pointers
+    # operands that would run past the end of the address space cannot exist
+    ((MAX_DIM, 4, 4, A_, 1 << 40, B_, 4, C_, 4), INVALID),       # A: 2^31 rows of 2^40 floats
+    ((4, 4, MAX_DIM, A_, MAX_DIM, B_, 1 << 40, C_, 4), INVALID),  # B
+    ((MAX_DIM, 4, 4, A_, 4, B_, 4, C_, 1 << 40), INVALID),       # C
+    ((MAX_DIM, 4, 0, A_, 1, B_, 4, C_, 1 << 40), INVALID),       # C, even when K = 0 only zeroes it
 ]
 
 
@@ -231,6 +236,8 @@ TRANSPOSE_CASES = [
     ((4, 8, A_, 1 << 41, B_, 4), UNSUPPORTED),
     ((0, 8, A_, 8, B_, 1), tg.TGEMM_SUCCESS),       # M = 0: nothing to do
     ((4, 0, 0, 1, 0, 4), tg.TGEMM_SUCCESS),         # N = 0 ignores pointers
+    ((MAX_DIM, 4, A_, 1 << 40, B_, MAX_DIM), INVALID),  # A runs past the address space
+    ((4, MAX_DIM, A_, MAX_DIM, B_, 1 << 40), INVALID),  # B likewise
 ]
 
 
@@ -271,6 +278,8 @@ HOST_CASES = [
     ((4, 4, 4, A_, 4, B_, 4, A_ + 8, 4, W_, 1 << 20, 0), INVALID),    # C overlaps A
     ((MAX_DIM + 1, 4, 4, A_, 4, B_, 4, C_, 4, W_, 1 << 20, 0), UNSUPPORTED),
     ((0, 4, 4, A_, 4, B_, 4, C_, 4, 0, 0, 0), tg.TGEMM_SUCCESS),      # M = 0: nothing to do
+    ((MAX_DIM, 4, 4, A_, 1 << 40, B_, 4, C_, 4, W_, 1 << 20, 0), INVALID),  # A past the address space
+    ((MAX_DIM, 4, 0, A_, 1, B_, 4, C_, 1 << 40, 0, 0, 0), INVALID),        # C likewise, K = 0
 ]
 
 

@@ -21,11 +21,17 @@ constexpr int64_t kMaxDim = ((int64_t)1 << 31) - ((int64_t)1 << 16);
 int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
 // Byte range [lo, hi) spanned by a rows×cols row-major operand with leading
-// dimension ld (rows, cols >= 1).
-void span(const void *p, int64_t rows, int64_t cols, int64_t ld, uintptr_t &lo, uintptr_t &hi)
+// dimension ld (rows, cols >= 1).  False if the range runs past the end of
+// the address space (rows up to 2^31 times ld up to 2^40 can): no such
+// operand exists, so the caller reports an invalid argument.
+bool span(const void *p, int64_t rows, int64_t cols, int64_t ld, uintptr_t &lo, uintptr_t &hi)
 {
     lo = reinterpret_cast<uintptr_t>(p);
-    hi = lo + (uintptr_t)(((rows - 1) * ld + cols) * (int64_t)sizeof(float));
+    const unsigned __int128 end =
+        (unsigned __int128)lo + ((unsigned __int128)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * sizeof(float);
+    if (end > (unsigned __int128)UINTPTR_MAX) return false;
+    hi = (uintptr_t)end;
+    return true;
 }
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
@@ -49,6 +55,8 @@ tgemm_status_t validate(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const
         return TGEMM_SUCCESS;
     }
     if (C == nullptr || reinterpret_cast<uintptr_t>(C) % alignof(float)) return TGEMM_ERROR_INVALID_VALUE;
+    uintptr_t a0, a1, b0, b1, c0, c1;
+    if (!span(C, M, N, ldc, c0, c1)) return TGEMM_ERROR_INVALID_VALUE;
     if (K == 0) {
         quick = Quick::kZeroFill;
         return TGEMM_SUCCESS;
@@ -56,10 +64,8 @@ tgemm_status_t validate(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const
     if (A == nullptr || B == nullptr) return TGEMM_ERROR_INVALID_VALUE;
     if (reinterpret_cast<uintptr_t>(A) % alignof(float) || reinterpret_cast<uintptr_t>(B) % alignof(float))
         return TGEMM_ERROR_INVALID_VALUE;
-    uintptr_t a0, a1, b0, b1, c0, c1;
-    span(A, ta ? K : M, ta ? M : K, lda, a0, a1);
-    span(B, tb ? N : K, tb ? K : N, ldb, b0, b1);
-    span(C, M, N, ldc, c0, c1);
+    if (!span(A, ta ? K : M, ta ? M : K, lda, a0, a1) || !span(B, tb ? N : K, tb ? K : N, ldb, b0, b1))
+        return TGEMM_ERROR_INVALID_VALUE;
     if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return TGEMM_ERROR_INVALID_VALUE;
     return TGEMM_SUCCESS;
 }
@@ -271,8 +277,7 @@ tgemm_status_t tgemm_transpose(int64_t M, int64_t N, const float *A, int64_t lda
         reinterpret_cast<uintptr_t>(B) % alignof(float))
         return TGEMM_ERROR_INVALID_VALUE;
     uintptr_t a0, a1, b0, b1;
-    span(A, M, N, lda, a0, a1);
-    span(B, N, M, ldb, b0, b1);
+    if (!span(A, M, N, lda, a0, a1) || !span(B, N, M, ldb, b0, b1)) return TGEMM_ERROR_INVALID_VALUE;
     if (overlaps(a0, a1, b0, b1)) return TGEMM_ERROR_INVALID_VALUE;
     const bool vec4 = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
     return from_hip(tgemm::launch_transpose(kind, tgemm::TransposeArgs{(int)M, (int)N, A, lda, B, ldb, vec4},

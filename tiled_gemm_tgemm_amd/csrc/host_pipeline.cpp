@@ -56,11 +56,25 @@ Layout layout(int64_t M, int64_t N, int64_t K, int64_t panel_rows)
     return l;
 }
 
+// End (one past the last byte) of a rows×cols host operand with leading
+// dimension ld, in 128 bits: rows up to 2^31 times ld up to 2^40 overflows 64.
+unsigned __int128 end_of(const void *p, int64_t rows, int64_t cols, int64_t ld)
+{
+    return (unsigned __int128)reinterpret_cast<uintptr_t>(p) +
+           ((unsigned __int128)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * sizeof(float);
+}
+
+// Whether the operand runs past the end of the address space (no such operand exists).
+bool beyond(const void *p, int64_t rows, int64_t cols, int64_t ld)
+{
+    return end_of(p, rows, cols, ld) > (unsigned __int128)UINTPTR_MAX;
+}
+
 bool overlaps(const void *p, int64_t rows, int64_t cols, int64_t ld, const void *q, int64_t qrows, int64_t qcols,
               int64_t qld)
 {
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)(((rows - 1) * ld + cols) * 4);
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + (uintptr_t)(((qrows - 1) * qld + qcols) * 4);
+    const unsigned __int128 a0 = reinterpret_cast<uintptr_t>(p), a1 = end_of(p, rows, cols, ld);
+    const unsigned __int128 b0 = reinterpret_cast<uintptr_t>(q), b1 = end_of(q, qrows, qcols, qld);
     return a0 < b1 && b0 < a1;
 }
 
@@ -87,12 +101,13 @@ tgemm_status_t tgemm_sgemm_host(int64_t M, int64_t N, int64_t K, const float *A,
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return TGEMM_ERROR_NOT_SUPPORTED;
     if (lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40 || ldc > (int64_t)1 << 40) return TGEMM_ERROR_NOT_SUPPORTED;
     if (M == 0 || N == 0) return TGEMM_SUCCESS;
-    if (C == nullptr || misaligned(C)) return TGEMM_ERROR_INVALID_VALUE;
+    if (C == nullptr || misaligned(C) || beyond(C, M, N, ldc)) return TGEMM_ERROR_INVALID_VALUE;
     if (K == 0) {  // the empty sum, written on the host: no device work at all
         for (int64_t i = 0; i < M; ++i) memset(C + i * ldc, 0, (size_t)N * sizeof(float));
         return TGEMM_SUCCESS;
     }
     if (A == nullptr || B == nullptr || misaligned(A) || misaligned(B)) return TGEMM_ERROR_INVALID_VALUE;
+    if (beyond(A, M, K, lda) || beyond(B, K, N, ldb)) return TGEMM_ERROR_INVALID_VALUE;
     if (overlaps(C, M, N, ldc, A, M, K, lda) || overlaps(C, M, N, ldc, B, K, N, ldb))
         return TGEMM_ERROR_INVALID_VALUE;
     const Layout l = layout(M, N, K, panel_rows);
