@@ -64,11 +64,39 @@ TRANSPOSE_SOURCE = "tiled_gemm_tgemm_amd/csrc/transpose.hip"
 KERNEL_SOURCES = ["tiled_gemm_tgemm_amd/csrc/mfma_sgemm.hip", "tiled_gemm_tgemm_amd/csrc/mfma_common.h"]
 
 
+def code_of(path: str) -> bytes:
+    """A C++/HIP source with its comments and blank lines removed, so that a
+    change of wording alone does not make a counter record stale.  Removes
+    // and /* */ comments outside string and character literals."""
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [l.rstrip() for l in "".join(out).split("\n")]
+    return "\n".join(l for l in lines if l.strip()).encode()
+
+
 def kernel_source_hash() -> str:
+    """SHA-256 of the product kernel's code (comments aside)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        h.update(code_of(os.path.join(ROOT, rel)))
     return h.hexdigest()
 
 
@@ -245,8 +273,7 @@ def transpose_traffic_for(workload_name: str, kernel: str):
         return None
     with open(TRANSPOSE_TRAFFIC_RECORD) as f:
         rec = json.load(f)
-    with open(os.path.join(ROOT, TRANSPOSE_SOURCE), "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
+    digest = hashlib.sha256(code_of(os.path.join(ROOT, TRANSPOSE_SOURCE))).hexdigest()
     if rec.get("kernel_source_sha256") != digest or rec.get("kernel") != kernel:
         return None
     entry = rec.get("workloads", {}).get(workload_name)

@@ -112,6 +112,28 @@ __device__ __forceinline__ void mfma_phase(f32x16 (&acc)[FM][FN], const float *a
     }
 }
 
+// Scheduling hints for one k-group's MFMA block: NX instructions of class MX
+// and then NY of class MY are spread evenly among its NM matrix-core
+// instructions (classes as for __builtin_amdgcn_sched_group_barrier: 0x008
+// MFMA, 0x020 VMEM read, 0x100 DS read, 0x200 DS write).
+template <int NM, int NX, int MX, int NY, int MY, int ID>
+__device__ __forceinline__ void interleave()
+{
+    constexpr int n = NX + NY;
+    constexpr int per = n == 0 ? NM : (NM / n > 0 ? NM / n : 1);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, per, ID);
+        __builtin_amdgcn_sched_group_barrier(MX, 1, ID);
+    }
+#pragma unroll
+    for (int i = 0; i < NY; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, per, ID);
+        __builtin_amdgcn_sched_group_barrier(MY, 1, ID);
+    }
+    if constexpr (NM > per * n) __builtin_amdgcn_sched_group_barrier(0x008, NM - per * n, ID);
+}
+
 // Accumulator register r of lane (l32, half) in block (i, j) is C row
 // 8*(r/4) + 4*half + r%4 and column l32 of that block.  Rows >= M and columns
 // >= N are not written.

@@ -21,26 +21,37 @@
 //   partial phase of K masks A's columns explicitly; B's rows past K fall
 //   outside its extent on their own.
 // * LDS holds two stages and registers hold two more phases in flight.
-//   Phase p computes from stage p%2; then phase p+1, whose loads were issued
-//   two phases earlier, is written from registers to the other stage, the
-//   loads of phase p+3 are issued into the registers just freed, and one
-//   barrier ends the phase.  That barrier covers both of the pages' reasons
-//   to synchronise (page 1, "__syncthreads( )"): the stage about to be read
-//   is complete, and the stage about to be refilled was last read before the
-//   previous barrier.  A load thus has two phases of matrix-core work (its
-//   own wavefront's and, with two work-groups per compute unit, the other
-//   wavefront's on the same SIMD) to arrive, so a miss in L2 rarely stalls
-//   the LDS write.  The two register sets alternate, so the main loop is
-//   unrolled by two and has no branches; the last phases (the partial K
-//   phase among them) run in a tail loop.  Measured on MI355X at 8192³
-//   (4096³), bit-identical results, by how many phases ahead of its
-//   computation a phase's loads are issued: one (the next phase only, issued
-//   after the matrix-core block with its issue priority raised) 92.4%
-//   (91.0%) of peak; two (one register set) 93.5% (92.3%); three (this
-//   schedule) 94.7% (93.4%); four needs a third register set, which spills
-//   at this tile and is no better at the smaller ones.  With loads in flight
-//   across phases, raising the priority of the matrix-core block costs 4-5
-//   points, so it is not raised.
+//   Phase p computes from stage p%2; phase p+1, whose loads were issued two
+//   phases earlier, is written from registers to the other stage; the loads
+//   of phase p+3 are issued into the registers just freed; and there is one
+//   barrier per phase.  That barrier covers both of the pages' reasons to
+//   synchronise (page 1, "__syncthreads( )"): the stage about to be read is
+//   complete, and the stage about to be refilled is read no more.  A load
+//   has two phases of matrix-core work (its own wavefront's and, with two
+//   work-groups per compute unit, the other wavefront's on the same SIMD)
+//   to arrive, so a miss in L2 rarely stalls the LDS write.  The two register
+//   sets alternate, so the main loop is unrolled by two and has no branches;
+//   the last phases (the partial K phase among them) run in a tail loop.
+//   Measured on MI355X at 8192³ (4096³), bit-identical results, by how many
+//   phases ahead of its computation a phase's loads are issued: one (the
+//   next phase only, issued after the matrix-core block with its issue
+//   priority raised) 92.4% (91.0%) of peak; two (one register set) 93.5%
+//   (92.3%); three (this ring) 94.7% (93.4%); four needs a third register
+//   set, which spills at this tile and is no better at the smaller ones.
+//   With loads in flight across phases, raising the priority of the
+//   matrix-core block costs 4-5 points, so it is not raised.
+// * Within a phase, two schedules.  Plain (4-byte loads): all k-groups,
+//   then the write, the loads and the barrier.  Interleaved (16-byte loads):
+//   each k-group's MFMAs cover the reads of the next group's fragments; the
+//   first group's also cover the write of phase p+1; the barrier sits before
+//   the last k-group, whose fragments are already in registers, so the last
+//   group's MFMAs cover the reads of phase p+1's first fragments and the
+//   loads.  Every LDS access then has a k-group of MFMAs to complete in.
+//   The compiler is told the interleave (which memory instruction after how
+//   many MFMAs): without that it bunches them and the same code is 4-5
+//   points slower; with it, 95.6-96.2% of peak at 8192³ against 94.4% for
+//   the plain schedule.  With 4-byte loads (24 per phase) the interleaved
+//   schedule needs more registers than two work-groups per CU allow.
 // * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
@@ -175,6 +186,9 @@ struct Cfg {
     static constexpr int GROUP_M = GROUP_M_;
     static constexpr int OCC = OCC_;                   // wavefronts per SIMD to budget registers for
     static constexpr int NS = 2;                       // register sets of staged loads (see the kernel)
+    // the interleaved phase schedule (see the kernel) for 16-byte loads; with
+    // 4-byte loads it needs more registers than two work-groups per CU allow
+    static constexpr bool INTERLEAVED = VEC == 4;
     static constexpr bool TA = TA_, TB = TB_;          // operands stored transposed
     static constexpr int NT = kWave * WM * WN;         // threads per work-group
     static constexpr int TM = BM / WM, TN = BN / WN;   // wavefront sub-tile
@@ -242,15 +256,10 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         for (int j = 0; j < G::FN; ++j)
             b_frag[g][j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, g, half);
     }
-    auto compute = [&] __device__(int stage) {
-        const float *s = lds + stage * G::STAGE;
-        mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, s, s + G::A_STAGE,
-                                                                               a_frag, b_frag);
-    };
-
     const int full = K / G::BK;                  // phases with all BK values of k
     const int nphase = full + (K % G::BK != 0);  // plus a shorter last one
-    // set s: issue the loads of phase r (the partial one if r == full) / write it to LDS stage r % 2
+    // register set s: issue the loads of phase r (`last`: the shorter one) /
+    // write phase r to LDS stage r % 2
     auto issue = [&] __device__(int s, int r, bool last) {
         la[s].issue(a_tile, lda, r * G::BK, K, rows_valid, last);
         lb[s].issue(b_tile, ldb, r * G::BK, K, cols_valid, last);
@@ -261,36 +270,89 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         lb[s].store(st + G::A_STAGE);
     };
 
+    typedef mfma::Fragments<G::FM, G::FN, LA::KC, LA::S, LB::KC, LB::S> Frag;
+    constexpr int NG = G::BK / 8;                                             // k-groups per phase
+    constexpr int NM = 4 * G::FM * G::FN;                                     // MFMAs per k-group
+    constexpr int RD = G::FM * (LA::KC ? 1 : 2) + G::FN * (LB::KC ? 1 : 2);  // LDS reads per k-group
+    constexpr int WR = LA::L + LB::L;                                         // LDS writes, loads per phase
+    static_assert(NG % 2 == 0, "phase depth must be a multiple of 16");
+    Frag f[2];
+    auto rd = [&] __device__(Frag &fr, int stage, int g) {
+        const float *st = lds + stage * G::STAGE;
+        fr.read(st, st + G::A_STAGE, a_frag[g], b_frag[g]);
+    };
+    // One phase r, computed from LDS stage r % 2 with register set s holding
+    // phase r+1.  next: phase r+1 exists (write it, then the barrier); load:
+    // phase r+1+NS exists (issue its loads into set s), load_last: it is the
+    // shorter one.
+    auto phase = [&] __device__(int s, int r, bool next, bool load, bool load_last) {
+        if constexpr (G::INTERLEAVED) {
+            // k-group g's MFMAs run while group g+1's fragments are read
+            // (f[0] holds group 0 on entry); the first group's MFMAs also
+            // cover the writes of phase r+1 into the other stage.  The one
+            // barrier comes before the last group, whose fragments are
+            // already in registers: it certifies that stage r+1 is complete
+            // and that stage r is read no more, so the last group's MFMAs
+            // cover the reads of phase r+1's first group and the loads of
+            // phase r+1+NS.  The compiler is told how to interleave each
+            // group (sched_group_barrier); without that it bunches the
+            // memory instructions and the kernel runs slower than the plain
+            // schedule.
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                if (g + 1 < NG) {
+                    rd(f[(g + 1) & 1], r & 1, g + 1);
+                    if (g == 0 && next) store(s, r + 1);
+                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                    if (g == 0)
+                        mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
+                    else
+                        mfma::interleave<NM, RD, 0x100, 0, 0x200, 1>();
+                } else {
+                    if (next) {
+                        __syncthreads();
+                        rd(f[0], (r + 1) & 1, 0);
+                    }
+                    if (load) issue(s, r + 1 + G::NS, load_last);
+                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                    mfma::interleave<NM, RD, 0x100, WR, 0x020, 2>();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // all k-groups (each group's MFMAs cover the next group's reads),
+            // then the write of phase r+1, the loads of phase r+1+NS and the
+            // barrier
+            const float *st = lds + (r & 1) * G::STAGE;
+            mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, st, st + G::A_STAGE,
+                                                                                   a_frag, b_frag);
+            if (next) {
+                store(s, r + 1);
+                if (load) issue(s, r + 1 + G::NS, load_last);
+                __syncthreads();
+            }
+        }
+    };
+
     issue(G::NS - 1, 0, full == 0);
     store(G::NS - 1, 0);
 #pragma unroll
     for (int s = 0; s < G::NS; ++s)
         if (s + 1 < nphase) issue(s, s + 1, s + 1 == full);
     __syncthreads();
+    if constexpr (G::INTERLEAVED) rd(f[0], 0, 0);
     int p = 0;
 #pragma unroll 1
     for (; p + 2 * G::NS < full; p += G::NS) {  // every phase loaded in here is a full one
 #pragma unroll
-        for (int s = 0; s < G::NS; ++s) {
-            compute((p + s) & 1);
-            store(s, p + s + 1);
-            issue(s, p + s + 1 + G::NS, false);
-            __syncthreads();
-        }
+        for (int s = 0; s < G::NS; ++s) phase(s, p + s, true, true, false);
     }
 #pragma unroll 1
     for (; p < nphase; p += G::NS) {
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) {
             const int r = p + s;
-            if (r < nphase) {
-                compute(r & 1);
-                if (r + 1 < nphase) {
-                    store(s, r + 1);
-                    if (r + 1 + G::NS < nphase) issue(s, r + 1 + G::NS, r + 1 + G::NS == full);
-                    __syncthreads();
-                }
-            }
+            if (r < nphase) phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, r + 1 + G::NS == full);
         }
     }
 
@@ -364,12 +426,12 @@ typedef Shape<64, 64, 32, 1, 8, 4> Small1;
 // Efficiencies measured on MI355X: 256 tiles with K = 8192 (one work-group per
 // CU) and four full rounds with K = 4096, as fractions of the matrix-core peak.
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.86, 0.94),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.83, 0.90),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.70, 0.86),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.93, 0.95),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.93, 0.95),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.68, 0.90),
     TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.81, 0.93),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.78, 0.90),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.63, 0.85),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.77, 0.90),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.63, 0.88),
 };
 
 }  // namespace
