@@ -60,7 +60,7 @@ def test_static_queries(lib):
     n = tg.tgemm_mfma_variant_count()
     assert n >= 6
     names = tg.variant_names()
-    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_(w\dx\d|s\dd\d)_vec[14](_flat)?", x) for x in names)
+    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_(w\dx\d(s\d)?|s\dd\d)_vec[14](_flat)?", x) for x in names)
     assert tg.tgemm_mfma_variant_name(n) is None and tg.tgemm_mfma_variant_name(-1) is None
     for st in range(4):
         assert tg.tgemm_status_string(st)
@@ -204,6 +204,7 @@ def test_variant_choice(lib):
     assert chosen(2500, 2500, 2500) == "m64n64k32_w2x2_vec4"    # 272 µs vs 305 for 128×128
     assert chosen(6144, 6144, 6144) == "m128n128k32_w2x2_vec4"
     assert chosen(256, 256, 8192) == "m32n32k8_s8d8_vec4"
+    assert chosen(1024, 1024, 8192) == "m64n64k32_w2x2s4_vec4"    # K split in the work-group: 155 vs 165 µs
     assert chosen(300, 300, 300, lda=1 << 24).endswith("_flat")   # lda beyond 32-bit offsets
     assert chosen(3000, 5000, 1000).endswith("vec4")
     assert chosen(7, 5, 3).endswith("vec1")          # K, N not multiples of 4

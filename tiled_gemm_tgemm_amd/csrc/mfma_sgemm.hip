@@ -52,6 +52,16 @@
 //   points slower; with it, 95.6-96.2% of peak at 8192³ against 94.4% for
 //   the plain schedule.  With 4-byte loads (24 per phase) the interleaved
 //   schedule needs more registers than two work-groups per CU allow.
+// * K split inside a work-group (the 64×64 configurations with KS = 2 or 4):
+//   on shapes with too few tiles to give every SIMD more than one wavefront
+//   (about 1024³, or small M·N with long K), the work-group holds KS groups
+//   of wavefronts, each running the pipeline above over its own slice of K
+//   (a whole number of phases; the last slice shorter) with its own LDS
+//   stages and registers.  Every slice runs the same phases, so the barriers
+//   stay uniform; reads past a slice's end return zero.  At the end the
+//   slices' sums meet in LDS and slice 0 adds them in slice order and writes
+//   C, so the result does not depend on timing.  Measured on MI355X:
+//   1024×1024×8192 210 → 156 µs, 1024³ 29 → 24 µs with four slices.
 // * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
@@ -180,9 +190,10 @@ struct Loader {
 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int VEC_, int GROUP_M_, int OCC_, bool TA_,
-          bool TB_>
+          bool TB_, int KS_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, VEC = VEC_;
+    static constexpr int KS = KS_;                     // K slices per work-group (see the kernel)
     static constexpr int GROUP_M = GROUP_M_;
     static constexpr int OCC = OCC_;                   // wavefronts per SIMD to budget registers for
     static constexpr int NS = 2;                       // register sets of staged loads (see the kernel)
@@ -190,14 +201,16 @@ struct Cfg {
     // 4-byte loads it needs more registers than two work-groups per CU allow
     static constexpr bool INTERLEAVED = VEC == 4;
     static constexpr bool TA = TA_, TB = TB_;          // operands stored transposed
-    static constexpr int NT = kWave * WM * WN;         // threads per work-group
+    static constexpr int NTS = kWave * WM * WN;        // threads per K slice
+    static constexpr int NT = NTS * KS;                // threads per work-group
     static constexpr int TM = BM / WM, TN = BN / WN;   // wavefront sub-tile
     static constexpr int FM = TM / 32, FN = TN / 32;   // 32×32 blocks per wavefront
-    typedef Loader<!TA, BM, BK, VEC, NT> LA;           // A as stored is k-contiguous
-    typedef Loader<TB, BN, BK, VEC, NT> LB;            // B as stored is n-contiguous
+    typedef Loader<!TA, BM, BK, VEC, NTS> LA;          // A as stored is k-contiguous
+    typedef Loader<TB, BN, BK, VEC, NTS> LB;           // B as stored is n-contiguous
     static constexpr int A_STAGE = LA::WORDS;
     static constexpr int STAGE = A_STAGE + LB::WORDS;
-    static constexpr int LDS_WORDS = 2 * STAGE;
+    static constexpr int LDS_WORDS = 2 * STAGE * KS;   // two stages per K slice
+    static_assert(KS == 1 || (KS - 1) * NTS * FM * FN * 16 <= LDS_WORDS, "slice sums fit in LDS");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront sub-tile must be 32-aligned");
     static_assert(BK % 8 == 0, "phase depth must be a multiple of 8");
     static_assert(LDS_WORDS * 4 <= 160 * 1024, "LDS budget of one gfx950 CU");
@@ -221,7 +234,9 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int rows_valid = min(G::BM, M - m0), cols_valid = min(G::BN, N - n0);
 
-    const int t = threadIdx.x;
+    constexpr bool SPLIT = G::KS > 1;
+    const int ks = SPLIT ? (int)threadIdx.x / G::NTS : 0;                // K slice of this thread
+    const int t = SPLIT ? (int)threadIdx.x % G::NTS : (int)threadIdx.x;  // index within the slice
     const int lane = t % kWave, wave = t / kWave;
     const int wm = wave / G::WN, wn = wave % G::WN;
     const int l32 = lane % 32, half = lane / 32;
@@ -256,16 +271,39 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         for (int j = 0; j < G::FN; ++j)
             b_frag[g][j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, g, half);
     }
-    const int full = K / G::BK;                  // phases with all BK values of k
-    const int nphase = full + (K % G::BK != 0);  // plus a shorter last one
+    // K range [kb, ke) of this thread's slice; `full` phases hold BK values
+    // of k, `nphase` phases in all, and phase r is `cut` (its k range reaches
+    // past ke: A's columns there are masked) from r = full on.  With K split,
+    // slices are kchunk long (a whole number of phases), the last shorter;
+    // every slice runs the same phases, so barriers match: `full` counts the
+    // phases that are whole in every slice, `nphase` the first slice's, and
+    // reads past a slice's end return zero.
+    int kb = 0, ke = K, full, nphase;
+    if constexpr (SPLIT) {
+        const int kchunk = ((K + G::KS - 1) / G::KS + G::BK - 1) / G::BK * G::BK;
+        kb = min(K, ks * kchunk);
+        ke = min(K, kb + kchunk);
+        full = max(0, K - (G::KS - 1) * kchunk) / G::BK;
+        nphase = kchunk / G::BK;
+    } else {
+        full = K / G::BK;
+        nphase = full + (K % G::BK != 0);
+    }
+    float *const slds = SPLIT ? lds + ks * 2 * G::STAGE : lds;  // this slice's two stages
+    auto cut = [&] __device__(int r) -> bool {
+        if constexpr (SPLIT)
+            return kb + (r + 1) * G::BK > ke;
+        else
+            return r == full;
+    };
     // register set s: issue the loads of phase r (`last`: the shorter one) /
     // write phase r to LDS stage r % 2
     auto issue = [&] __device__(int s, int r, bool last) {
-        la[s].issue(a_tile, lda, r * G::BK, K, rows_valid, last);
-        lb[s].issue(b_tile, ldb, r * G::BK, K, cols_valid, last);
+        la[s].issue(a_tile, lda, kb + r * G::BK, ke, rows_valid, last);
+        lb[s].issue(b_tile, ldb, kb + r * G::BK, ke, cols_valid, last);
     };
     auto store = [&] __device__(int s, int r) {
-        float *st = lds + (r & 1) * G::STAGE;
+        float *st = slds + (r & 1) * G::STAGE;
         la[s].store(st);
         lb[s].store(st + G::A_STAGE);
     };
@@ -278,7 +316,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
     static_assert(NG % 2 == 0, "phase depth must be a multiple of 16");
     Frag f[2];
     auto rd = [&] __device__(Frag &fr, int stage, int g) {
-        const float *st = lds + stage * G::STAGE;
+        const float *st = slds + stage * G::STAGE;
         fr.read(st, st + G::A_STAGE, a_frag[g], b_frag[g]);
     };
     // One phase r, computed from LDS stage r % 2 with register set s holding
@@ -323,7 +361,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
             // all k-groups (each group's MFMAs cover the next group's reads),
             // then the write of phase r+1, the loads of phase r+1+NS and the
             // barrier
-            const float *st = lds + (r & 1) * G::STAGE;
+            const float *st = slds + (r & 1) * G::STAGE;
             mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, st, st + G::A_STAGE,
                                                                                    a_frag, b_frag);
             if (next) {
@@ -334,11 +372,11 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         }
     };
 
-    issue(G::NS - 1, 0, full == 0);
+    issue(G::NS - 1, 0, cut(0));
     store(G::NS - 1, 0);
 #pragma unroll
     for (int s = 0; s < G::NS; ++s)
-        if (s + 1 < nphase) issue(s, s + 1, s + 1 == full);
+        if (s + 1 < nphase) issue(s, s + 1, cut(s + 1));
     __syncthreads();
     if constexpr (G::INTERLEAVED) rd(f[0], 0, 0);
     int p = 0;
@@ -352,10 +390,37 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) {
             const int r = p + s;
-            if (r < nphase) phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, r + 1 + G::NS == full);
+            if (r < nphase) phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, cut(r + 1 + G::NS));
         }
     }
 
+    if constexpr (G::KS > 1) {
+        // the slices' sums meet in LDS (the stages are free once every
+        // wavefront has passed the first barrier) and are added in slice order
+        constexpr int PER = G::FM * G::FN * 16;  // accumulators per lane
+        __syncthreads();
+        if (ks > 0) {
+            float *red = lds + ((ks - 1) * (G::NTS / kWave) + wave) * PER * kWave + lane;
+#pragma unroll
+            for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[((i * G::FN + j) * 16 + r) * kWave] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (ks > 0) return;
+#pragma unroll
+        for (int q = 1; q < G::KS; ++q) {
+            const float *red = lds + ((q - 1) * (G::NTS / kWave) + wave) * PER * kWave + lane;
+#pragma unroll
+            for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * G::FN + j) * 16 + r) * kWave];
+        }
+    }
     mfma::store_c<G::FM, G::FN>(acc, C, ldc, M, N, m0 + wm * G::TM, n0 + wn * G::TN, half, l32);
 }
 
@@ -376,7 +441,9 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream)
 template <class G>
 constexpr int wg_per_cu()
 {
-    return (160 * 1024) / (G::LDS_WORDS * 4) < G::OCC ? (160 * 1024) / (G::LDS_WORDS * 4) : G::OCC;
+    constexpr int by_lds = (160 * 1024) / (G::LDS_WORDS * 4);
+    constexpr int by_waves = G::OCC * 4 / (G::WM * G::WN * G::KS);  // OCC wavefronts per SIMD
+    return by_lds < by_waves ? by_lds : by_waves;
 }
 
 // Buffer offsets are 32-bit and kept below 2^31: a slot's offset spans at
@@ -388,11 +455,12 @@ constexpr int64_t max_ld()
     return ((((int64_t)1 << 31) - 16) / 4 - L::COLS) / L::ROWS;
 }
 
-// One tile shape in its four operand orders (NN, TN, NT, TT).
-template <int BM, int BN, int BK, int VEC, int GM, int OCC>
+// One tile shape (with KS slices of K per work-group) in its four operand
+// orders (NN, TN, NT, TT).
+template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1>
 struct Shape {
     template <bool TA, bool TB>
-    using C = Cfg<BM, BN, BK, 2, 2, VEC, GM, OCC, TA, TB>;
+    using C = Cfg<BM, BN, BK, 2, 2, VEC, GM, OCC, TA, TB, KS>;
     static hipError_t launch(const GemmArgs &g, hipStream_t stream)
     {
         switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
@@ -411,8 +479,12 @@ typedef Shape<64, 64, 32, 4, 8, 4> Small4;
 typedef Shape<256, 128, 16, 1, 4, 2> Large1;
 typedef Shape<128, 128, 32, 1, 8, 2> Mid1;
 typedef Shape<64, 64, 32, 1, 8, 4> Small1;
+typedef Shape<64, 64, 32, 4, 8, 4, 2> Small4x2;  // K split over two groups of wavefronts
+typedef Shape<64, 64, 32, 4, 8, 4, 4> Small4x4;  // ... over four
+typedef Shape<64, 64, 32, 1, 8, 4, 2> Small1x2;
+typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
 
-#define TGEMM_VARIANT(name, S, alone, full)                                                         \
+#define TGEMM_VARIANT(name, S, alone, full, round)                                                  \
     {                                                                                                \
         name, S::template C<false, false>::BM, S::template C<false, false>::BN,                     \
             S::template C<false, false>::BK, S::template C<false, false>::VEC,                      \
@@ -420,18 +492,28 @@ typedef Shape<64, 64, 32, 1, 8, 4> Small1;
             max_ld<typename S::template C<false, false>::LA>(),                                     \
             max_ld<typename S::template C<false, false>::LB>(),                                     \
             max_ld<typename S::template C<true, false>::LA>(),                                      \
-            max_ld<typename S::template C<false, true>::LB>(), true, alone, full, 7000.0, &S::launch \
+            max_ld<typename S::template C<false, true>::LB>(), true, alone, full, round, &S::launch  \
     }
 
 // Efficiencies measured on MI355X: 256 tiles with K = 8192 (one work-group per
 // CU) and four full rounds with K = 4096, as fractions of the matrix-core peak.
+// For the K-split configurations, efficiencies and the fixed cost per round
+// (which carries the slices' final sum) were chosen against a sweep of 23
+// shapes from 128³ to 8192³ so that the model's pick is the measured fastest
+// or within 1.5% of it; the split wins only where K is long for the number
+// of tiles (1024×1024×8192: 155 µs against 165 µs unsplit).  The 4-byte-load
+// flavours keep the measured ratio to the 16-byte ones.
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.93, 0.95),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.93, 0.95),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.68, 0.90),
-    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.81, 0.93),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.77, 0.90),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.63, 0.88),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.93, 0.95, 7000.0),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.93, 0.95, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.68, 0.90, 7000.0),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.81, 0.93, 7000.0),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.77, 0.90, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.63, 0.88, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2s2_vec4", Small4x2, 0.60, 0.72, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2s4_vec4", Small4x4, 0.72, 0.72, 10000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2s2_vec1", Small1x2, 0.44, 0.55, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2s4_vec1", Small1x4, 0.55, 0.55, 10000.0),
 };
 
 }  // namespace
