@@ -355,6 +355,7 @@ def time_transpose(w, kernel: str, steps: int, warmup: int, warmup_seconds: floa
 
 def transpose_main(args, props):
     import numpy as np
+    import torch
 
     from tiled_gemm_tgemm_amd import workloads as wl
 
@@ -389,7 +390,8 @@ def transpose_main(args, props):
         "copy_reference": {"what": "device-to-device copy of the same M·N floats",
                            "gbs": round(gbs(m["copy_ms"]), 1), "ms": round(m["copy_ms"], 4),
                            "transpose_over_copy": round(m["copy_ms"] / m["kernel_ms"], 4)},
-        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+                   "hip": torch.version.hip},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -499,7 +501,8 @@ def host_main(args, props):
             "transfer_floor_ms": round(max(in_bytes / (h2d_gbs * 1e9), out_bytes / (d2h_gbs * 1e9)) * 1e3, 3),
             "results_equal_serial": same,
         },
-        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+                   "hip": torch.version.hip},
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -562,7 +565,8 @@ def main():
         "kernel_ms": {"mean": round(m["kernel_ms"], 4), "min": round(m["kernel_ms_min"], 4),
                       "median": round(m["kernel_ms_median"], 4), "p90": round(m["kernel_ms_p90"], 4)},
         "algorithmic_hbm_gbs": round(w.algorithmic_bytes / (m["kernel_ms"] * 1e-3) / 1e9, 1),
-        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+                   "hip": torch.version.hip},
     }
     # the vendor library computes the plain product; compare only what it computes
     vendor = not args.no_vendor and args.kernel == "auto" and not args.cold
