@@ -310,6 +310,51 @@ def test_phase_ring_tail_integer_exact(K):
             assert_exact(run(A, B, "mfma", variant=v), Pi, f"{name} K={K}")
 
 
+def test_persistent_grid_integer_exact_with_guard_bands():
+    """More tiles than the chip holds at once for every configuration
+    (4100² is 561 tiles of 256×128, 1089 of 128², 4225 of 64², so each
+    work-group of the persistent grid runs several), ragged in M and N, with
+    enough whole phases at either depth (16 and 32) for the main loop's
+    whole-phase loads and a shorter last phase.  A and B sit in NaN-filled
+    wider buffers and C inside sentinels: a NaN in C means a load outside
+    the operands, a changed sentinel a store outside C.  Integers, exact."""
+    M, N, K = 4100, 4100, 196
+    A, B = int_inputs(M, N, K, 4100)
+    Pi = oracle.gemm_i64(A, B)
+    for v, name in [(None, "auto")] + list(enumerate(variants())):
+        if v is not None and not runnable(name, M, N, K):
+            continue
+        log(f"persistent grid {M}x{N}x{K}: {name}")
+        _, Av = guarded(A, 3, 8, float("nan"))
+        _, Bv = guarded(B, 5, 4, float("nan"))
+        Cbig, Cv = guarded(np.zeros((M, N), np.float32), 2, 4, 12345.0)
+        if v is None:
+            tg.sgemm(Av, Bv, out=Cv)
+        else:
+            tg.sgemm(Av, Bv, out=Cv, kernel="mfma", variant=v)
+        torch.cuda.synchronize()
+        big = Cbig.cpu().numpy()
+        assert_exact(big[:M, :N], Pi, name)
+        outside = np.ones(big.shape, bool)
+        outside[:M, :N] = False
+        assert np.all(big[outside] == 12345.0), f"{name} wrote outside C"
+
+
+def test_persistent_grid_transposed_integer_exact():
+    """The persistent grid with operands stored transposed (the main
+    configuration in all four orders), ragged and with a shorter last
+    phase.  Integers, exact."""
+    M, N, K = 4100, 4100, 100
+    A, B = int_inputs(M, N, K, 4101)
+    Pi = oracle.gemm_i64(A, B)
+    for ta, tb in OPS:
+        dA, dB = stored(A, ta), stored(B, tb)
+        log(f"persistent grid transposed ta={ta} tb={tb}")
+        C = tg.sgemm(dA, dB)
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), Pi, f"auto ta={ta} tb={tb}")
+
+
 def test_leading_dimension_beyond_buffer_offsets():
     """lda past what 32-bit buffer offsets cover: tgemm_sgemm runs the 64-bit
     pointer configuration, buffer configurations refuse it."""

@@ -15,17 +15,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kWave = 64;
 constexpr int kXcds = 8;
 
-// Map the hardware work-group id to a C tile (tm, tn).  The hardware deals
-// ids round-robin to the eight XCDs (each with its own L2): XCD x holds ids
-// x, x+8, x+16, ...  Each XCD is given the contiguous run of logical ids
-// that starts after the runs of XCDs 0..x-1, and logical ids walk groups of
-// group_m tile rows column by column, so the work-groups resident on one XCD
-// cover a compact block of C tiles and share A rows and B columns in its L2.
-// Both steps are bijections on [0, tiles_m * tiles_n).
-__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
+// Map tile id wg of nwg = tiles_m * tiles_n (the hardware work-group id when
+// the grid has one work-group per tile) to a C tile (tm, tn).  The hardware
+// deals work-group ids round-robin to the eight XCDs (each with its own L2):
+// XCD x holds ids x, x+8, x+16, ...; a persistent grid whose size is a
+// multiple of 8 keeps tile id ≡ work-group id (mod 8).  Each XCD is given the
+// contiguous run of logical ids that starts after the runs of XCDs 0..x-1,
+// and logical ids walk groups of group_m tile rows column by column, so the
+// work-groups resident on one XCD cover a compact block of C tiles and share
+// A rows and B columns in its L2.  Both steps are bijections on [0, nwg).
+__device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int group_m, int &tm, int &tn,
+                                        int wg = blockIdx.x, int nwg = gridDim.x)
 {
-    const int nwg = gridDim.x;
-    const int wg = blockIdx.x;
     const int q = nwg / kXcds, r = nwg % kXcds;
     const int x = wg % kXcds;
     const int logical = wg / kXcds + x * q + (x < r ? x : r);

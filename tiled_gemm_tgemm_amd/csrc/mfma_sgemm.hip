@@ -86,6 +86,8 @@
 //   layout.  No operand is transposed on the way (page 1, section
 //   [Coalescing], "Corner Turning": load in the coalesced order, read on chip
 //   in the order the arithmetic needs).
+#include <atomic>
+
 #include "mfma_common.h"
 #include "tgemm_kernels.h"
 
@@ -182,6 +184,20 @@ struct Loader {
         }
     }
 
+    // Issue the loads of a whole phase (every k of it below the end of the
+    // summed range).  The extent then only has to exclude the lanes outside
+    // the matrix, which carry kOutside, so the descriptor takes the largest
+    // extent and only its base moves with k0: two scalar additions a phase
+    // instead of the exact extent's 64-bit arithmetic.
+    __device__ __forceinline__ void issue_whole(const float *tile, int64_t ld, int k0)
+    {
+        const float *base = KC ? tile + k0 : tile + (int64_t)k0 * ld;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < L; ++i) reg[i] = Vec<VEC>::load(rs, off[i]);
+    }
+
     __device__ __forceinline__ void store(float *stage) const
     {
 #pragma unroll
@@ -229,213 +245,221 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
 
     const int tiles_m = (M + G::BM - 1) / G::BM;
     const int tiles_n = (N + G::BN - 1) / G::BN;
-    int tm, tn;
-    mfma::tile_of(tiles_m, tiles_n, G::GROUP_M, tm, tn);
-    const int m0 = tm * G::BM, n0 = tn * G::BN;
-    const int rows_valid = min(G::BM, M - m0), cols_valid = min(G::BN, N - n0);
+    const int ntiles = tiles_m * tiles_n;
+    // the grid holds at most as many work-groups as the chip holds at once;
+    // each one takes tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        int tm, tn;
+        mfma::tile_of(tiles_m, tiles_n, G::GROUP_M, tm, tn, tile, ntiles);
+        const int m0 = tm * G::BM, n0 = tn * G::BN;
+        const int rows_valid = min(G::BM, M - m0), cols_valid = min(G::BN, N - n0);
 
-    constexpr bool SPLIT = G::KS > 1;
-    const int ks = SPLIT ? (int)threadIdx.x / G::NTS : 0;                // K slice of this thread
-    const int t = SPLIT ? (int)threadIdx.x % G::NTS : (int)threadIdx.x;  // index within the slice
-    const int lane = t % kWave, wave = t / kWave;
-    const int wm = wave / G::WN, wn = wave % G::WN;
-    const int l32 = lane % 32, half = lane / 32;
+        constexpr bool SPLIT = G::KS > 1;
+        const int ks = SPLIT ? (int)threadIdx.x / G::NTS : 0;                // K slice of this thread
+        const int t = SPLIT ? (int)threadIdx.x % G::NTS : (int)threadIdx.x;  // index within the slice
+        const int lane = t % kWave, wave = t / kWave;
+        const int wm = wave / G::WN, wn = wave % G::WN;
+        const int l32 = lane % 32, half = lane / 32;
 
-    // NS register sets of staged loads: phase r travels in set (r - 1) mod NS
-    LA la[G::NS];
-    LB lb[G::NS];
-    la[0].init(t, lda, rows_valid);
-    lb[0].init(t, ldb, cols_valid);
+        // NS register sets of staged loads: phase r travels in set (r - 1) mod NS
+        LA la[G::NS];
+        LB lb[G::NS];
+        la[0].init(t, lda, rows_valid);
+        lb[0].init(t, ldb, cols_valid);
 #pragma unroll
-    for (int s = 1; s < G::NS; ++s) {
-        la[s] = la[0];
-        lb[s] = lb[0];
-    }
-    // operand pointers at (m0, 0) and (n0, 0) in their own storage order
-    const float *a_tile = A + (LA::KC ? (int64_t)m0 * lda : (int64_t)m0);
-    const float *b_tile = B + (LB::KC ? (int64_t)n0 * ldb : (int64_t)n0);
+        for (int s = 1; s < G::NS; ++s) {
+            la[s] = la[0];
+            lb[s] = lb[0];
+        }
+        // operand pointers at (m0, 0) and (n0, 0) in their own storage order
+        const float *a_tile = A + (LA::KC ? (int64_t)m0 * lda : (int64_t)m0);
+        const float *b_tile = B + (LB::KC ? (int64_t)n0 * ldb : (int64_t)n0);
 
-    f32x16 acc[G::FM][G::FN];
-#pragma unroll
-    for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
-
-    int a_frag[G::BK / 8][G::FM], b_frag[G::BK / 8][G::FN];
-#pragma unroll
-    for (int g = 0; g < G::BK / 8; ++g) {
+        f32x16 acc[G::FM][G::FN];
 #pragma unroll
         for (int i = 0; i < G::FM; ++i)
-            a_frag[g][i] = mfma::frag_offset<LA::KC, LA::S>(wm * G::TM + i * 32 + l32, g, half);
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j)
-            b_frag[g][j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, g, half);
-    }
-    // K range [kb, ke) of this thread's slice; `full` phases hold BK values
-    // of k, `nphase` phases in all, and phase r is `cut` (its k range reaches
-    // past ke: A's columns there are masked) from r = full on.  With K split,
-    // slices are kchunk long (a whole number of phases), the last shorter;
-    // every slice runs the same phases, so barriers match: `full` counts the
-    // phases that are whole in every slice, `nphase` the first slice's, and
-    // reads past a slice's end return zero.
-    int kb = 0, ke = K, full, nphase;
-    if constexpr (SPLIT) {
-        const int kchunk = ((K + G::KS - 1) / G::KS + G::BK - 1) / G::BK * G::BK;
-        kb = min(K, ks * kchunk);
-        ke = min(K, kb + kchunk);
-        full = max(0, K - (G::KS - 1) * kchunk) / G::BK;
-        nphase = kchunk / G::BK;
-    } else {
-        full = K / G::BK;
-        nphase = full + (K % G::BK != 0);
-    }
-    float *const slds = SPLIT ? lds + ks * 2 * G::STAGE : lds;  // this slice's two stages
-    auto cut = [&] __device__(int r) -> bool {
-        if constexpr (SPLIT)
-            return kb + (r + 1) * G::BK > ke;
-        else
-            return r == full;
-    };
-    // register set s: issue the loads of phase r (`last`: the shorter one) /
-    // write phase r to LDS stage r % 2
-    auto issue = [&] __device__(int s, int r, bool last) {
-        la[s].issue(a_tile, lda, kb + r * G::BK, ke, rows_valid, last);
-        lb[s].issue(b_tile, ldb, kb + r * G::BK, ke, cols_valid, last);
-    };
-    auto store = [&] __device__(int s, int r) {
-        float *st = slds + (r & 1) * G::STAGE;
-        la[s].store(st);
-        lb[s].store(st + G::A_STAGE);
-    };
+            for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-    typedef mfma::Fragments<G::FM, G::FN, LA::KC, LA::S, LB::KC, LB::S> Frag;
-    constexpr int NG = G::BK / 8;                                             // k-groups per phase
-    constexpr int NM = 4 * G::FM * G::FN;                                     // MFMAs per k-group
-    constexpr int RD = G::FM * (LA::KC ? 1 : 2) + G::FN * (LB::KC ? 1 : 2);  // LDS reads per k-group
-    constexpr int WR = LA::L + LB::L;                                         // LDS writes, loads per phase
-    static_assert(NG % 2 == 0, "phase depth must be a multiple of 16");
-    Frag f[2];
-    auto rd = [&] __device__(Frag &fr, int stage, int g) {
-        const float *st = slds + stage * G::STAGE;
-        fr.read(st, st + G::A_STAGE, a_frag[g], b_frag[g]);
-    };
-    // One phase r, computed from LDS stage r % 2 with register set s holding
-    // phase r+1.  next: phase r+1 exists (write it, then the barrier); load:
-    // phase r+1+NS exists (issue its loads into set s), load_last: it is the
-    // shorter one.
-    auto phase = [&] __device__(int s, int r, bool next, bool load, bool load_last) {
-        if constexpr (G::INTERLEAVED) {
-            // k-group g's MFMAs run while group g+1's fragments are read
-            // (f[0] holds group 0 on entry); the first group's MFMAs also
-            // cover the writes of phase r+1 into the other stage.  The one
-            // barrier comes before the last group, whose fragments are
-            // already in registers: it certifies that stage r+1 is complete
-            // and that stage r is read no more, so the last group's MFMAs
-            // cover the reads of phase r+1's first group and the loads of
-            // phase r+1+NS.  The compiler is told how to interleave each
-            // group (sched_group_barrier); without that it bunches the
-            // memory instructions and the kernel runs slower than the plain
-            // schedule.
+        int a_frag[G::BK / 8][G::FM], b_frag[G::BK / 8][G::FN];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                if (g + 1 < NG) {
-                    rd(f[(g + 1) & 1], r & 1, g + 1);
-                    if (g == 0 && next) store(s, r + 1);
-                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
-                    if (g == 0)
-                        mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
-                    else
-                        mfma::interleave<NM, RD, 0x100, 0, 0x200, 1>();
-                } else {
-                    if (next) {
-                        __syncthreads();
-                        rd(f[0], (r + 1) & 1, 0);
-                    }
-                    if (load) issue(s, r + 1 + G::NS, load_last);
-                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
-                    mfma::interleave<NM, RD, 0x100, WR, 0x020, 2>();
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int g = 0; g < G::BK / 8; ++g) {
+#pragma unroll
+            for (int i = 0; i < G::FM; ++i)
+                a_frag[g][i] = mfma::frag_offset<LA::KC, LA::S>(wm * G::TM + i * 32 + l32, g, half);
+#pragma unroll
+            for (int j = 0; j < G::FN; ++j)
+                b_frag[g][j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, g, half);
+        }
+        // K range [kb, ke) of this thread's slice; `full` phases hold BK values
+        // of k, `nphase` phases in all, and phase r is `cut` (its k range reaches
+        // past ke: A's columns there are masked) from r = full on.  With K split,
+        // slices are kchunk long (a whole number of phases), the last shorter;
+        // every slice runs the same phases, so barriers match: `full` counts the
+        // phases that are whole in every slice, `nphase` the first slice's, and
+        // reads past a slice's end return zero.
+        int kb = 0, ke = K, full, nphase;
+        if constexpr (SPLIT) {
+            const int kchunk = ((K + G::KS - 1) / G::KS + G::BK - 1) / G::BK * G::BK;
+            kb = min(K, ks * kchunk);
+            ke = min(K, kb + kchunk);
+            full = max(0, K - (G::KS - 1) * kchunk) / G::BK;
+            nphase = kchunk / G::BK;
         } else {
-            // all k-groups (each group's MFMAs cover the next group's reads),
-            // then the write of phase r+1, the loads of phase r+1+NS and the
-            // barrier
-            const float *st = slds + (r & 1) * G::STAGE;
-            mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, st, st + G::A_STAGE,
-                                                                                   a_frag, b_frag);
-            if (next) {
-                store(s, r + 1);
-                if (load) issue(s, r + 1 + G::NS, load_last);
-                __syncthreads();
+            full = K / G::BK;
+            nphase = full + (K % G::BK != 0);
+        }
+        float *const slds = SPLIT ? lds + ks * 2 * G::STAGE : lds;  // this slice's two stages
+        auto cut = [&] __device__(int r) -> bool {
+            if constexpr (SPLIT)
+                return kb + (r + 1) * G::BK > ke;
+            else
+                return r == full;
+        };
+        // register set s: issue the loads of phase r (`last`: the shorter one) /
+        // write phase r to LDS stage r % 2
+        auto issue = [&] __device__(int s, int r, bool last) {
+            la[s].issue(a_tile, lda, kb + r * G::BK, ke, rows_valid, last);
+            lb[s].issue(b_tile, ldb, kb + r * G::BK, ke, cols_valid, last);
+        };
+        auto issue_whole = [&] __device__(int s, int r) {
+            la[s].issue_whole(a_tile, lda, kb + r * G::BK);
+            lb[s].issue_whole(b_tile, ldb, kb + r * G::BK);
+        };
+        auto store = [&] __device__(int s, int r) {
+            float *st = slds + (r & 1) * G::STAGE;
+            la[s].store(st);
+            lb[s].store(st + G::A_STAGE);
+        };
+
+        typedef mfma::Fragments<G::FM, G::FN, LA::KC, LA::S, LB::KC, LB::S> Frag;
+        constexpr int NG = G::BK / 8;                                             // k-groups per phase
+        constexpr int NM = 4 * G::FM * G::FN;                                     // MFMAs per k-group
+        constexpr int RD = G::FM * (LA::KC ? 1 : 2) + G::FN * (LB::KC ? 1 : 2);  // LDS reads per k-group
+        constexpr int WR = LA::L + LB::L;                                         // LDS writes, loads per phase
+        static_assert(NG % 2 == 0, "phase depth must be a multiple of 16");
+        Frag f[2];
+        auto rd = [&] __device__(Frag &fr, int stage, int g) {
+            const float *st = slds + stage * G::STAGE;
+            fr.read(st, st + G::A_STAGE, a_frag[g], b_frag[g]);
+        };
+        // One phase r, computed from LDS stage r % 2 with register set s holding
+        // phase r+1.  next: phase r+1 exists (write it, then the barrier); load:
+        // phase r+1+NS exists (issue its loads into set s), load_last: it is the
+        // shorter one; whole: it is a whole phase (issue_whole).
+        auto phase = [&] __device__(int s, int r, bool next, bool load, bool load_last, bool whole) {
+            auto issue_next = [&] __device__() {
+                if (whole)
+                    issue_whole(s, r + 1 + G::NS);
+                else if (load)
+                    issue(s, r + 1 + G::NS, load_last);
+            };
+            if constexpr (G::INTERLEAVED) {
+                // k-group g's MFMAs run while group g+1's fragments are read
+                // (f[0] holds group 0 on entry); the first group's MFMAs also
+                // cover the writes of phase r+1 into the other stage.  The one
+                // barrier comes before the last group, whose fragments are
+                // already in registers: it certifies that stage r+1 is complete
+                // and that stage r is read no more, so the last group's MFMAs
+                // cover the reads of phase r+1's first group and the loads of
+                // phase r+1+NS.  The compiler is told how to interleave each
+                // group (sched_group_barrier); without that it bunches the
+                // memory instructions and the kernel runs slower than the plain
+                // schedule.
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    if (g + 1 < NG) {
+                        rd(f[(g + 1) & 1], r & 1, g + 1);
+                        if (g == 0 && next) store(s, r + 1);
+                        mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                        if (g == 0)
+                            mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
+                        else
+                            mfma::interleave<NM, RD, 0x100, 0, 0x200, 1>();
+                    } else {
+                        if (next) {
+                            __syncthreads();
+                            rd(f[0], (r + 1) & 1, 0);
+                        }
+                        issue_next();
+                        mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                        mfma::interleave<NM, RD, 0x100, WR, 0x020, 2>();
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // all k-groups (each group's MFMAs cover the next group's reads),
+                // then the write of phase r+1, the loads of phase r+1+NS and the
+                // barrier
+                const float *st = slds + (r & 1) * G::STAGE;
+                mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, st, st + G::A_STAGE,
+                                                                                       a_frag, b_frag);
+                if (next) {
+                    store(s, r + 1);
+                    issue_next();
+                    __syncthreads();
+                }
+            }
+        };
+
+        issue(G::NS - 1, 0, cut(0));
+        store(G::NS - 1, 0);
+            // phases past the last one are loaded too (a buffer extent that ends
+        // inside the operand's valid rows or is empty, and never written to
+        // LDS): with the loads unconditional the compiler's count of loads
+        // in flight at the loop head is exact, and each LDS write waits for
+        // its own phase's loads only
+#pragma unroll
+        for (int s = 0; s < G::NS; ++s) issue(s, s + 1, cut(s + 1));
+        __syncthreads();
+        if constexpr (G::INTERLEAVED) rd(f[0], 0, 0);
+        int p = 0;
+#pragma unroll 1
+        for (; p + 2 * G::NS < full; p += G::NS) {  // every phase loaded in here is a full one
+#pragma unroll
+            for (int s = 0; s < G::NS; ++s) phase(s, p + s, true, true, false, true);
+        }
+#pragma unroll 1
+        for (; p < nphase; p += G::NS) {
+#pragma unroll
+            for (int s = 0; s < G::NS; ++s) {
+                const int r = p + s;
+                if (r < nphase) phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, cut(r + 1 + G::NS), false);
             }
         }
-    };
 
-    issue(G::NS - 1, 0, cut(0));
-    store(G::NS - 1, 0);
+        if constexpr (G::KS > 1) {
+            // the slices' sums meet in LDS (the stages are free once every
+            // wavefront has passed the first barrier) and are added in slice order
+            constexpr int PER = G::FM * G::FN * 16;  // accumulators per lane
+            __syncthreads();
+            if (ks > 0) {
+                float *red = lds + ((ks - 1) * (G::NTS / kWave) + wave) * PER * kWave + lane;
 #pragma unroll
-    for (int s = 0; s < G::NS; ++s)
-        if (s + 1 < nphase) issue(s, s + 1, cut(s + 1));
-    __syncthreads();
-    if constexpr (G::INTERLEAVED) rd(f[0], 0, 0);
-    int p = 0;
-#pragma unroll 1
-    for (; p + 2 * G::NS < full; p += G::NS) {  // every phase loaded in here is a full one
+                for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-        for (int s = 0; s < G::NS; ++s) phase(s, p + s, true, true, false);
-    }
-#pragma unroll 1
-    for (; p < nphase; p += G::NS) {
+                    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-        for (int s = 0; s < G::NS; ++s) {
-            const int r = p + s;
-            if (r < nphase) phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, cut(r + 1 + G::NS));
+                        for (int r = 0; r < 16; ++r) red[((i * G::FN + j) * 16 + r) * kWave] = acc[i][j][r];
+            }
+            __syncthreads();
+            if (ks > 0) return;  // with K split the grid is one work-group per tile
+#pragma unroll
+            for (int q = 1; q < G::KS; ++q) {
+                const float *red = lds + ((q - 1) * (G::NTS / kWave) + wave) * PER * kWave + lane;
+#pragma unroll
+                for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * G::FN + j) * 16 + r) * kWave];
+            }
         }
+        mfma::store_c<G::FM, G::FN>(acc, C, ldc, M, N, m0 + wm * G::TM, n0 + wn * G::TN, half, l32);
+        // the next tile's first write into LDS waits until every wavefront
+        // is done reading this tile's last stage
+        if (tile + (int)gridDim.x < ntiles) __syncthreads();
     }
-
-    if constexpr (G::KS > 1) {
-        // the slices' sums meet in LDS (the stages are free once every
-        // wavefront has passed the first barrier) and are added in slice order
-        constexpr int PER = G::FM * G::FN * 16;  // accumulators per lane
-        __syncthreads();
-        if (ks > 0) {
-            float *red = lds + ((ks - 1) * (G::NTS / kWave) + wave) * PER * kWave + lane;
-#pragma unroll
-            for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) red[((i * G::FN + j) * 16 + r) * kWave] = acc[i][j][r];
-        }
-        __syncthreads();
-        if (ks > 0) return;
-#pragma unroll
-        for (int q = 1; q < G::KS; ++q) {
-            const float *red = lds + ((q - 1) * (G::NTS / kWave) + wave) * PER * kWave + lane;
-#pragma unroll
-            for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * G::FN + j) * 16 + r) * kWave];
-        }
-    }
-    mfma::store_c<G::FM, G::FN>(acc, C, ldc, M, N, m0 + wm * G::TM, n0 + wn * G::TN, half, l32);
-}
-
-template <class G>
-hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream)
-{
-    const int64_t tiles = (int64_t)((g.M + G::BM - 1) / G::BM) * ((g.N + G::BN - 1) / G::BN);
-    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
-    int M = g.M, N = g.N, K = g.K;
-    const float *A = g.A, *B = g.B;
-    float *C = g.C;
-    int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
-    void *args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&mfma_sgemm_kernel<G>),
-                           dim3((unsigned)tiles), dim3(G::NT), args, 0, stream);
 }
 
 template <class G>
@@ -444,6 +468,50 @@ constexpr int wg_per_cu()
     constexpr int by_lds = (160 * 1024) / (G::LDS_WORDS * 4);
     constexpr int by_waves = G::OCC * 4 / (G::WM * G::WN * G::KS);  // OCC wavefronts per SIMD
     return by_lds < by_waves ? by_lds : by_waves;
+}
+
+// Compute units of the current device, read once per device (0 if the query
+// fails).  Every thread that reads it first stores the same value.
+int compute_units()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0)
+            return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Without a K split the grid is persistent: at most as many work-groups as
+// the chip holds at once (a multiple of the 8 XCDs when the CU count is),
+// each looping over tiles.  A grid of one work-group per tile, dealt in
+// rounds by the hardware, measured 2-4% slower from the third round on
+// (8192³: 150.3 against 151.7 TFLOP/s; 12288×4096×4096: 148.8 against
+// 150.7): later rounds start a work-group beside one half-way through its
+// tile, and the two then share the SIMDs unevenly.  With K split the grid is
+// one work-group per tile (those shapes have few tiles).
+template <class G>
+hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream)
+{
+    const int64_t tiles = (int64_t)((g.M + G::BM - 1) / G::BM) * ((g.N + G::BN - 1) / G::BN);
+    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    int64_t grid = tiles;
+    if constexpr (G::KS == 1) {
+        const int64_t slots = (int64_t)compute_units() * wg_per_cu<G>();
+        if (slots > 0 && slots < tiles) grid = slots;
+    }
+    int M = g.M, N = g.N, K = g.K;
+    const float *A = g.A, *B = g.B;
+    float *C = g.C;
+    int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
+    void *args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&mfma_sgemm_kernel<G>),
+                           dim3((unsigned)grid), dim3(G::NT), args, 0, stream);
 }
 
 // Buffer offsets are 32-bit and kept below 2^31: a slot's offset spans at
