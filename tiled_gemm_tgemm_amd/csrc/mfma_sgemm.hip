@@ -13,13 +13,25 @@
 //   4 lanes × 16 bytes cover a 64-byte A row segment, 32 lanes a 512-byte B
 //   row.
 // * The copies are buffer loads: each phase rebases a buffer descriptor on the
-//   slice's first element with the exact byte extent of what remains of the
-//   operand, and every lane keeps a fixed 32-bit offset.  Reads past the
-//   extent return zero in hardware, and lanes whose row (A) or column (B)
-//   lies outside the matrix carry an offset beyond any extent, so edge tiles
-//   need no per-element tests and no load leaves the operand.  Only the last,
-//   partial phase of K masks A's columns explicitly; B's rows past K fall
-//   outside its extent on their own.
+//   slice's first element, and every lane keeps a fixed 32-bit offset.  Lanes
+//   whose row (A) or column (B) lies outside the matrix carry an offset
+//   beyond any extent, which the hardware answers with zero, so edge tiles
+//   need no per-element tests and no load leaves the operand.  Whole phases
+//   (the main loop) need nothing more: their descriptor takes the largest
+//   extent and only its base moves, two scalar additions a phase.  The last
+//   phases (the tail loop) carry the exact extent of what remains of the
+//   operand; the partial phase of K masks A's columns explicitly, and B's
+//   rows past K fall outside its extent on their own.  Recomputing the exact
+//   extent every phase, as the tail does, costs 64-bit scalar arithmetic and
+//   vector compares among the matrix-core instructions: 1.5-2% at 4096³,
+//   and 9% at 1024³.
+// * The grid is persistent (configurations without a K split): at most as
+//   many work-groups as the chip holds at once, each looping over tiles
+//   blockIdx.x, blockIdx.x + gridDim.x, ...  With one work-group per tile
+//   dealt in rounds by the hardware, the lean loop above lost 2-4% from the
+//   third round on (a work-group starting beside one half-way through its
+//   tile, the two sharing the SIMDs unevenly); persistent, it gains at every
+//   size measured.
 // * LDS holds two stages and registers hold two more phases in flight.
 //   Phase p computes from stage p%2; phase p+1, whose loads were issued two
 //   phases earlier, is written from registers to the other stage; the loads
@@ -33,13 +45,15 @@
 //   sets alternate, so the main loop is unrolled by two and has no branches;
 //   the last phases (the partial K phase among them) run in a tail loop.
 //   Measured on MI355X at 8192³ (4096³), bit-identical results, by how many
-//   phases ahead of its computation a phase's loads are issued: one (the
-//   next phase only, issued after the matrix-core block with its issue
-//   priority raised) 92.4% (91.0%) of peak; two (one register set) 93.5%
-//   (92.3%); three (this ring) 94.7% (93.4%); four needs a third register
-//   set, which spills at this tile and is no better at the smaller ones.
-//   With loads in flight across phases, raising the priority of the
-//   matrix-core block costs 4-5 points, so it is not raised.
+//   phases ahead of its computation a phase's loads are issued (before the
+//   lean loads and the persistent grid): one (the next phase only, issued
+//   after the matrix-core block with its issue priority raised) 92.4%
+//   (91.0%) of peak; two (one register set) 93.5% (92.3%); three (this
+//   ring) 94.7% (93.4%); four needs a third register set, which spills at
+//   this tile and is no better at the smaller ones.  With loads in flight
+//   across phases, raising the priority of the matrix-core block costs 4-5
+//   points, so it is not raised.  The loads' latency is not what is left:
+//   pointing every work-group at one cached tile gains 0.3%.
 // * Within a phase, two schedules.  Plain (4-byte loads): all k-groups,
 //   then the write, the loads and the barrier.  Interleaved (16-byte loads):
 //   each k-group's MFMAs cover the reads of the next group's fragments; the
@@ -50,7 +64,7 @@
 //   The compiler is told the interleave (which memory instruction after how
 //   many MFMAs): without that it bunches them and the same code is 4-5
 //   points slower; with it, 95.6-96.2% of peak at 8192³ against 94.4% for
-//   the plain schedule.  With 4-byte loads (24 per phase) the interleaved
+//   the plain schedule (97.4% with the lean loads and persistent grid).  With 4-byte loads (24 per phase) the interleaved
 //   schedule needs more registers than two work-groups per CU allow.
 // * K split inside a work-group (the 64×64 configurations with KS = 2 or 4):
 //   on shapes with too few tiles to give every SIMD more than one wavefront
@@ -61,7 +75,11 @@
 //   stay uniform; reads past a slice's end return zero.  At the end the
 //   slices' sums meet in LDS and slice 0 adds them in slice order and writes
 //   C, so the result does not depend on timing.  Measured on MI355X:
-//   1024×1024×8192 210 → 156 µs, 1024³ 29 → 24 µs with four slices.
+//   1024×1024×8192 210 → 156 µs, 1024³ 29 → 24 µs with four slices.  Since
+//   the whole-phase loads and the persistent grid, the unsplit 64×64 tile is
+//   ahead on every shape measured (1024×1024×8192: 133 against 148 µs;
+//   768×768×8192: 132 against 147 µs), so the selection model no longer
+//   picks these; they stay available through tgemm_sgemm_mfma.
 // * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
@@ -568,16 +586,20 @@ typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
 // For the K-split configurations, efficiencies and the fixed cost per round
 // (which carries the slices' final sum) were chosen against a sweep of 23
 // shapes from 128³ to 8192³ so that the model's pick is the measured fastest
-// or within 1.5% of it; the split wins only where K is long for the number
-// of tiles (1024×1024×8192: 155 µs against 165 µs unsplit).  The 4-byte-load
-// flavours keep the measured ratio to the 16-byte ones.
+// or within 1.5% of it.  With whole-phase loads and the persistent grid the
+// unsplit 64×64 configuration alone on a CU sped up most (1024×1024×8192:
+// 165 → 133 µs, now ahead of the four-way split at 148 µs), and its
+// efficiency alone was raised to match; a sweep of 20 shapes from 128³ to
+// 6144³ (square, ragged, long and short K) then finds the model's pick the
+// fastest or within 2% of it, apart from 128³ (5.5 µs against 5.1 µs).  The 4-byte-load flavours keep the
+// measured ratio to the 16-byte ones.
 const MfmaVariant kVariants[] = {
     TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.93, 0.95, 7000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.93, 0.95, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.68, 0.90, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.80, 0.90, 7000.0),
     TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.81, 0.93, 7000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.77, 0.90, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.63, 0.88, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.74, 0.88, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s2_vec4", Small4x2, 0.60, 0.72, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s4_vec4", Small4x4, 0.72, 0.72, 10000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s2_vec1", Small1x2, 0.44, 0.55, 7000.0),
