@@ -27,7 +27,12 @@
 //   runs of 128 contiguous bytes — whole cache lines in both directions,
 //   with no barrier and no bank conflicts.  Tiles that reach past M or N, and
 //   operands that are not 16-byte aligned with leading dimensions multiples
-//   of four, take the same mapping with single-word, masked accesses.
+//   of four, take the same mapping with single-word, masked accesses.  The
+//   output is written with non-temporal stores (B is not read back by the
+//   kernel): measured on MI355X, 16384² 5.33 → 5.39 TB/s, 8192² 4.44 → 6.31
+//   TB/s (B no longer displaces A from the 256 MB Infinity Cache), 4096²
+//   5.80 → 6.10 TB/s.  Non-temporal loads as well gain 1.7% more at 16384²
+//   but lose 30% at 8192² and 15% at 4096², so loads stay ordinary.
 #include "tgemm_kernels.h"
 
 namespace tgemm {
@@ -109,8 +114,8 @@ __global__ __launch_bounds__(kBlkThreads) void transpose_blocked_kernel(int M, i
         for (int p = 0; p < PC; ++p)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                *reinterpret_cast<f32x4 *>(B + (int64_t)(jb + 64 * p + s) * ldb + i0) =
-                    f32x4{r[p][0][s], r[p][1][s], r[p][2][s], r[p][3][s]};
+                __builtin_nontemporal_store(f32x4{r[p][0][s], r[p][1][s], r[p][2][s], r[p][3][s]},
+                                            reinterpret_cast<f32x4 *>(B + (int64_t)(jb + 64 * p + s) * ldb + i0));
         return;
     }
 #pragma unroll
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(kBlkThreads) void transpose_blocked_kernel(int M, i
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int i = i0 + s, j = j0 + q;
-                if (i < M && j < N) B[(int64_t)j * ldb + i] = r[s][q];
+                if (i < M && j < N) __builtin_nontemporal_store(r[s][q], B + (int64_t)j * ldb + i);
             }
     }
 }
