@@ -32,6 +32,9 @@ Reported:
   launch) over that time, against the MI355X dense fp32 matrix peak; the
   measured HBM traffic per launch comes from the committed rocprofv3 counter
   summary when it was taken on the current kernel source, else null;
+* engine_clock — the XCDs' mean engine clock read with amd-smi while the
+  product runs (after the timed steps), and the kernel's fraction of the
+  peak at that clock (CUs × 256 flops × clock); null without amd-smi;
 * cpu_baseline — the CPU oracle (float64, test infrastructure) timed on this
   host's cores on a bounded sample: whole rows of the same product;
 * vendor_blas — context only: torch.matmul in float32 with TF32 off (the ROCm
@@ -217,6 +220,61 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
         "tflops_wall": w.flops / (wall_ms * 1e-3) / 1e12,
         "tflops_kernel": w.flops / (kernel_ms * 1e-3) / 1e12,
     }
+
+
+def engine_clock(m, kernel: str, load_seconds: float = 2.0):
+    """Mean engine clock (GHz) of the XCDs while the product runs.  The same
+    call is launched back to back for `load_seconds`, then two child
+    `amd-smi metric -c --json` reads are taken while the launches go on; the
+    second is used (the tool reports a sampled value that can lag the load).
+    None where amd-smi is missing, fails, reports other than exactly one GPU,
+    or reports an XCD below its minimum clock (a sample of an idle engine)."""
+    import shutil
+    import subprocess
+
+    import torch
+
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if exe is None:
+        return None
+    call, _ = kernel_call(kernel)
+    A, B, C = m["A"], m["B"], m["C"]
+    n = 0
+
+    def busy_until(done):
+        nonlocal n
+        t0 = time.perf_counter()
+        while not done() and time.perf_counter() - t0 < 30.0:
+            call(A, B, C)
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+
+    t_load = time.perf_counter()
+    busy_until(lambda: time.perf_counter() - t_load >= load_seconds)
+    reading = None
+    for _ in range(2):
+        child = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
+                                 stderr=subprocess.DEVNULL, text=True)
+        busy_until(lambda: child.poll() is not None)
+        try:
+            out, _ = child.communicate(timeout=10)
+            reading = json.loads(out)["gpu_data"] if child.returncode == 0 else None
+        except (subprocess.TimeoutExpired, ValueError, KeyError, TypeError):
+            child.kill()
+            reading = None
+    torch.cuda.synchronize()
+    if not reading or len(reading) != 1:
+        return None
+    mhz = []
+    for k, v in reading[0].get("clock", {}).items():
+        if not k.startswith("gfx_") or not isinstance(v, dict) or not isinstance(v.get("clk"), dict):
+            continue
+        lo = v.get("min_clk")
+        if isinstance(lo, dict) and v["clk"]["value"] < lo["value"]:
+            return None
+        mhz.append(v["clk"]["value"])
+    return sum(mhz) / len(mhz) / 1e3 if mhz else None
 
 
 def vendor_blas(m, steps: int, warmup_seconds: float):
@@ -568,6 +626,18 @@ def main():
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "hip": torch.version.hip},
     }
+    if not args.cold:
+        ghz = engine_clock(m, args.kernel)
+        # flops per clock and CU: 256 on the fp32 matrix cores, 128 as unpacked vector FMAs
+        per_clk = 256 if bound == "mfma" else 128
+        at_clock = props.multi_processor_count * per_clk * ghz / 1e3 if ghz else None
+        line["engine_clock"] = None if ghz is None else {
+            "ghz": round(ghz, 3),
+            "what": "mean XCD engine clock from amd-smi, read after 2 s of the same call back to back "
+                    "(after the timed steps, while it still runs)",
+            "peak_at_this_clock": round(at_clock, 2),
+            "frac_of_peak_at_this_clock": round(achieved / at_clock, 4),
+        }
     # the vendor library computes the plain product; compare only what it computes
     vendor = not args.no_vendor and args.kernel == "auto" and not args.cold
     if vendor:

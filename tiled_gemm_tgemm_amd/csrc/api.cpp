@@ -100,8 +100,9 @@ bool runs(const tgemm::MfmaVariant &v, bool vec4, bool ta, bool tb, int64_t lda,
            ldb <= (tb ? v.max_ldb_t : v.max_ldb);
 }
 
-// Estimated time of a configuration in SIMD cycles.  Work-groups are dealt
-// to the 256 compute units in rounds of up to wg_per_cu per CU; the
+// Estimated time of a configuration in SIMD cycles.  Tiles are dealt to the
+// 256 compute units in rounds of up to wg_per_cu per CU (the persistent grid
+// runs them as each resident work-group's successive tiles); the
 // wavefronts of a work-group spread over the CU's 4 SIMDs, each retiring 64
 // flops a cycle at the efficiency measured for that many resident
 // work-groups (interpolated between alone and full).  The last round may
