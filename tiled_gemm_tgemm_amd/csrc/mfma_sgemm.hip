@@ -264,6 +264,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
     const int tiles_m = (M + G::BM - 1) / G::BM;
     const int tiles_n = (N + G::BN - 1) / G::BN;
     const int ntiles = tiles_m * tiles_n;
+    const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     // the grid holds at most as many work-groups as the chip holds at once;
     // each one takes tiles blockIdx.x, blockIdx.x + gridDim.x, ...
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -273,8 +274,16 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         const int rows_valid = min(G::BM, M - m0), cols_valid = min(G::BN, N - n0);
 
         constexpr bool SPLIT = G::KS > 1;
-        const int ks = SPLIT ? (int)threadIdx.x / G::NTS : 0;                // K slice of this thread
-        const int t = SPLIT ? (int)threadIdx.x % G::NTS : (int)threadIdx.x;  // index within the slice
+        // the lane-dependent offsets below are recomputed for every tile (a
+        // few integer operations) rather than kept in vector registers across
+        // the tile loop: the thread's index is rebuilt from the wavefront's
+        // index (a scalar) and the lane's position (v_mbcnt, fed an in-loop
+        // zero so that it is not hoisted)
+        unsigned zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+        const int tid = wave_id * kWave + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, zero));
+        const int ks = SPLIT ? tid / G::NTS : 0;    // K slice of this thread
+        const int t = SPLIT ? tid % G::NTS : tid;  // index within the slice
         const int lane = t % kWave, wave = t / kWave;
         const int wm = wave / G::WN, wn = wave % G::WN;
         const int l32 = lane % 32, half = lane / 32;
@@ -473,7 +482,15 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
                         for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * G::FN + j) * 16 + r) * kWave];
             }
         }
-        mfma::store_c<G::FM, G::FN>(acc, C, ldc, M, N, m0 + wm * G::TM, n0 + wn * G::TN, half, l32);
+        {
+            // this thread's place in the tile, rebuilt as at the tile's start
+            unsigned zero_c;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(zero_c));
+            const int lane_c = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, zero_c));
+            const int wave_c = (SPLIT ? (wave_id * kWave) % G::NTS : wave_id * kWave) / kWave;
+            mfma::store_c<G::FM, G::FN>(acc, C, ldc, M, N, m0 + (wave_c / G::WN) * G::TM,
+                                        n0 + (wave_c % G::WN) * G::TN, lane_c / 32, lane_c % 32);
+        }
         // the next tile's first write into LDS waits until every wavefront
         // is done reading this tile's last stage
         if (tile + (int)gridDim.x < ntiles) __syncthreads();
