@@ -54,9 +54,8 @@
 //   across phases, raising the priority of the matrix-core block costs 4-5
 //   points, so it is not raised.  The loads' latency is not what is left:
 //   pointing every work-group at one cached tile gains 0.3%.
-// * Within a phase, two schedules.  Plain (4-byte loads): all k-groups,
-//   then the write, the loads and the barrier.  Interleaved (16-byte loads):
-//   each k-group's MFMAs cover the reads of the next group's fragments; the
+// * Within a phase the memory work is interleaved with the MFMAs: each
+//   k-group's MFMAs cover the reads of the next group's fragments; the
 //   first group's also cover the write of phase p+1; the barrier sits before
 //   the last k-group, whose fragments are already in registers, so the last
 //   group's MFMAs cover the reads of phase p+1's first fragments and the
@@ -64,8 +63,13 @@
 //   The compiler is told the interleave (which memory instruction after how
 //   many MFMAs): without that it bunches them and the same code is 4-5
 //   points slower; with it, 95.6-96.2% of peak at 8192³ against 94.4% for
-//   the plain schedule (97.4% with the lean loads and persistent grid).  With 4-byte loads (24 per phase) the interleaved
-//   schedule needs more registers than two work-groups per CU allow.
+//   a plain schedule (all k-groups, then the write, the loads and the
+//   barrier); 97.4% with the lean loads and persistent grid.  With 4-byte
+//   loads (24 a phase at 256×128) two register sets spill at 256×128, so
+//   that configuration keeps one (loads two phases ahead); measured at
+//   8192³ with 4-byte loads forced: plain schedule 140.3 TFLOP/s,
+//   interleaved with one set 148.8, with two sets 134.3 (spilling); at
+//   128×128 two sets are ahead (139.3 against 133.3 plain).
 // * K split inside a work-group (the 64×64 configurations with KS = 2 or 4):
 //   on shapes with too few tiles to give every SIMD more than one wavefront
 //   (about 1024³, or small M·N with long K), the work-group holds KS groups
@@ -224,16 +228,14 @@ struct Loader {
 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int VEC_, int GROUP_M_, int OCC_, bool TA_,
-          bool TB_, int KS_ = 1>
+          bool TB_, int KS_ = 1, int NS_ = 2>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, VEC = VEC_;
     static constexpr int KS = KS_;                     // K slices per work-group (see the kernel)
     static constexpr int GROUP_M = GROUP_M_;
     static constexpr int OCC = OCC_;                   // wavefronts per SIMD to budget registers for
-    static constexpr int NS = 2;                       // register sets of staged loads (see the kernel)
-    // the interleaved phase schedule (see the kernel) for 16-byte loads; with
-    // 4-byte loads it needs more registers than two work-groups per CU allow
-    static constexpr bool INTERLEAVED = VEC == 4;
+    static constexpr int NS = NS_;                     // register sets of staged loads (see the kernel)
+    static_assert(NS == 1 || NS == 2, "one or two register sets");
     static constexpr bool TA = TA_, TB = TB_;          // operands stored transposed
     static constexpr int NTS = kWave * WM * WN;        // threads per K slice
     static constexpr int NT = NTS * KS;                // threads per work-group
@@ -381,57 +383,43 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
                 else if (load)
                     issue(s, r + 1 + G::NS, load_last);
             };
-            if constexpr (G::INTERLEAVED) {
-                // k-group g's MFMAs run while group g+1's fragments are read
-                // (f[0] holds group 0 on entry); the first group's MFMAs also
-                // cover the writes of phase r+1 into the other stage.  The one
-                // barrier comes before the last group, whose fragments are
-                // already in registers: it certifies that stage r+1 is complete
-                // and that stage r is read no more, so the last group's MFMAs
-                // cover the reads of phase r+1's first group and the loads of
-                // phase r+1+NS.  The compiler is told how to interleave each
-                // group (sched_group_barrier); without that it bunches the
-                // memory instructions and the kernel runs slower than the plain
-                // schedule.
+            // k-group g's MFMAs run while group g+1's fragments are read (f[0]
+            // holds group 0 on entry); the first group's MFMAs also cover the
+            // writes of phase r+1 into the other stage.  The one barrier comes
+            // before the last group, whose fragments are already in registers:
+            // it certifies that stage r+1 is complete and that stage r is read
+            // no more, so the last group's MFMAs cover the reads of phase r+1's
+            // first group and the loads of phase r+1+NS.  The compiler is told
+            // how to interleave each group (sched_group_barrier); without that
+            // it bunches the memory instructions and the kernel runs slower
+            // than a plain schedule (all groups, then the write, the loads and
+            // the barrier).
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    if (g + 1 < NG) {
-                        rd(f[(g + 1) & 1], r & 1, g + 1);
-                        if (g == 0 && next) store(s, r + 1);
-                        mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
-                        if (g == 0)
-                            mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
-                        else
-                            mfma::interleave<NM, RD, 0x100, 0, 0x200, 1>();
-                    } else {
-                        if (next) {
-                            __syncthreads();
-                            rd(f[0], (r + 1) & 1, 0);
-                        }
-                        issue_next();
-                        mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
-                        mfma::interleave<NM, RD, 0x100, WR, 0x020, 2>();
+            for (int g = 0; g < NG; ++g) {
+                if (g + 1 < NG) {
+                    rd(f[(g + 1) & 1], r & 1, g + 1);
+                    if (g == 0 && next) store(s, r + 1);
+                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                    if (g == 0)
+                        mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
+                    else
+                        mfma::interleave<NM, RD, 0x100, 0, 0x200, 1>();
+                } else {
+                    if (next) {
+                        __syncthreads();
+                        rd(f[0], (r + 1) & 1, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            } else {
-                // all k-groups (each group's MFMAs cover the next group's reads),
-                // then the write of phase r+1, the loads of phase r+1+NS and the
-                // barrier
-                const float *st = slds + (r & 1) * G::STAGE;
-                mfma::mfma_phase<G::FM, G::FN, G::BK, LA::KC, LA::S, LB::KC, LB::S>(acc, st, st + G::A_STAGE,
-                                                                                       a_frag, b_frag);
-                if (next) {
-                    store(s, r + 1);
                     issue_next();
-                    __syncthreads();
+                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                    mfma::interleave<NM, RD, 0x100, WR, 0x020, 2>();
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
         issue(G::NS - 1, 0, cut(0));
         store(G::NS - 1, 0);
-            // phases past the last one are loaded too (a buffer extent that ends
+        // phases past the last one are loaded too (a buffer extent that ends
         // inside the operand's valid rows or is empty, and never written to
         // LDS): with the loads unconditional the compiler's count of loads
         // in flight at the loop head is exact, and each LDS write waits for
@@ -439,7 +427,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) issue(s, s + 1, cut(s + 1));
         __syncthreads();
-        if constexpr (G::INTERLEAVED) rd(f[0], 0, 0);
+        rd(f[0], 0, 0);
         int p = 0;
 #pragma unroll 1
         for (; p + 2 * G::NS < full; p += G::NS) {  // every phase loaded in here is a full one
@@ -560,10 +548,10 @@ constexpr int64_t max_ld()
 
 // One tile shape (with KS slices of K per work-group) in its four operand
 // orders (NN, TN, NT, TT).
-template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1>
+template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1, int NS = 2>
 struct Shape {
     template <bool TA, bool TB>
-    using C = Cfg<BM, BN, BK, 2, 2, VEC, GM, OCC, TA, TB, KS>;
+    using C = Cfg<BM, BN, BK, 2, 2, VEC, GM, OCC, TA, TB, KS, NS>;
     static hipError_t launch(const GemmArgs &g, hipStream_t stream)
     {
         switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
@@ -579,7 +567,7 @@ struct Shape {
 typedef Shape<256, 128, 16, 4, 4, 2> Large4;
 typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
 typedef Shape<64, 64, 32, 4, 8, 4> Small4;
-typedef Shape<256, 128, 16, 1, 4, 2> Large1;
+typedef Shape<256, 128, 16, 1, 4, 2, 1, 1> Large1;  // one register set (two spill)
 typedef Shape<128, 128, 32, 1, 8, 2> Mid1;
 typedef Shape<64, 64, 32, 1, 8, 4> Small1;
 typedef Shape<64, 64, 32, 4, 8, 4, 2> Small4x2;  // K split over two groups of wavefronts
@@ -599,7 +587,11 @@ typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
     }
 
 // Efficiencies measured on MI355X: 256 tiles with K = 8192 (one work-group per
-// CU) and four full rounds with K = 4096, as fractions of the matrix-core peak.
+// CU) and four full rounds with K = 4096, as fractions of the matrix-core peak
+// (last measured with whole-phase loads, the persistent grid and the
+// interleaved schedule for 4-byte loads; the model's picks are unchanged from
+// the previous figures except on one misaligned shape, and on 8 shapes with
+// K, N not multiples of 4 its pick is the fastest 4-byte configuration).
 // For the K-split configurations, efficiencies and the fixed cost per round
 // (which carries the slices' final sum) were chosen against a sweep of 23
 // shapes from 128³ to 8192³ so that the model's pick is the measured fastest
@@ -611,12 +603,12 @@ typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
 // fastest or within 2% of it, apart from 128³ (5.5 µs against 5.1 µs).  The 4-byte-load flavours keep the
 // measured ratio to the 16-byte ones.
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.93, 0.95, 7000.0),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.93, 0.95, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.80, 0.90, 7000.0),
-    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.81, 0.93, 7000.0),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.77, 0.90, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.74, 0.88, 7000.0),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.97, 0.97, 7000.0),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.96, 0.96, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.91, 7000.0),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.93, 0.95, 7000.0),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.84, 0.89, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.69, 0.86, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s2_vec4", Small4x2, 0.60, 0.72, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s4_vec4", Small4x4, 0.72, 0.72, 10000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s2_vec1", Small1x2, 0.44, 0.55, 7000.0),
