@@ -118,6 +118,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-vendor", action="store_true",
                    help="skip timing the vendor BLAS (torch.matmul, fp32) beside the product")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="host threads for the cpu_baseline leg (0: the OpenMP default, all cores)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--op-a", choices=("N", "T"), default="N",
@@ -671,6 +673,10 @@ def main():
         line["copy_reference_bytes"] = 4 * n
         del src, dst
     if not args.no_cpu_baseline:
+        if args.cpu_threads > 0:
+            # the oracle's OpenMP regions share the runtime torch configured at
+            # import; this sets the thread count they run with
+            torch.set_num_threads(args.cpu_threads)
         line["cpu_baseline"] = cpu_baseline(m, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
