@@ -266,10 +266,17 @@ def engine_clock(m, kernel: str, load_seconds: float = 2.0):
             child.kill()
             reading = None
     torch.cuda.synchronize()
-    if not reading or len(reading) != 1:
+    return mean_engine_clock(reading)
+
+
+def mean_engine_clock(gpu_data):
+    """Mean of the XCD engine clocks (GHz) in amd-smi's `metric -c --json`
+    "gpu_data" list; None unless it holds exactly one GPU whose gfx_* clocks
+    are all at or above their minimum (below it, the engine was asleep)."""
+    if not gpu_data or len(gpu_data) != 1:
         return None
     mhz = []
-    for k, v in reading[0].get("clock", {}).items():
+    for k, v in gpu_data[0].get("clock", {}).items():
         if not k.startswith("gfx_") or not isinstance(v, dict) or not isinstance(v.get("clk"), dict):
             continue
         lo = v.get("min_clk")

@@ -1,0 +1,87 @@
+"""Host logic of bench.py that runs without a GPU: the one-GPU contract, the
+kernel-code hash that keys the committed traffic record, and the reading of
+amd-smi's clock report."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in (res.stdout + res.stderr)
+    assert not res.stdout.lstrip().startswith("{")  # no JSON line is printed
+
+
+def test_code_hash_ignores_comments_and_blank_lines(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    a.write_text('int f(int x) {\n    return x + 1;  // one\n}\n/* block */\nconst char *s = "// kept";\n')
+    b.write_text('// a new header comment\nint f(int x) {\n\n    return x + 1;  // reworded\n}\n'
+                 'const char *s = "// kept";\n')
+    assert bench.code_of(str(a)) == bench.code_of(str(b))
+    b.write_text('int f(int x) {\n    return x + 2;\n}\nconst char *s = "// kept";\n')
+    assert bench.code_of(str(a)) != bench.code_of(str(b))
+    # text inside string literals is code, not comment
+    b.write_text('int f(int x) {\n    return x + 1;\n}\nconst char *s = "// changed";\n')
+    assert bench.code_of(str(a)) != bench.code_of(str(b))
+
+
+def test_traffic_record_is_used_only_for_the_kernel_it_was_taken_on(tmp_path, monkeypatch):
+    record = {"kernel_source_sha256": bench.kernel_source_hash(), "kernel": "m256n128k16_w2x2_vec4",
+              "workloads": {"square8192_uniform": {"hbm_bytes_per_launch": 123456789}}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(record))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
+    assert bench.traffic_for("square8192_uniform", "m256n128k16_w2x2_vec4") == 123456789
+    assert bench.traffic_for("square4096_uniform", "m256n128k16_w2x2_vec4") is None
+    assert bench.traffic_for("square8192_uniform", "m128n128k32_w2x2_vec4") is None
+    record["kernel_source_sha256"] = "0" * 64
+    path.write_text(json.dumps(record))
+    assert bench.traffic_for("square8192_uniform", "m256n128k16_w2x2_vec4") is None
+
+
+def test_committed_traffic_record_matches_the_current_kernel():
+    """profiles/traffic.json must be re-measured whenever the product kernel's
+    code changes; otherwise bench.py reports roofline.traffic as null."""
+    with open(bench.TRAFFIC_RECORD) as f:
+        rec = json.load(f)
+    assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
+
+
+def _xcd(clk, lo=500):
+    return {"clk": {"value": clk, "unit": "MHz"}, "min_clk": {"value": lo, "unit": "MHz"},
+            "max_clk": {"value": 2400, "unit": "MHz"}}
+
+
+def _gpu(clocks):
+    c = {f"gfx_{i}": _xcd(v) for i, v in enumerate(clocks)}
+    c["mem_0"] = _xcd(2000, 2000)
+    c["vclk_0"] = {"clk": {"value": 59, "unit": "MHz"}, "min_clk": "N/A"}
+    return {"gpu": 0, "clock": c}
+
+
+def test_engine_clock_is_the_mean_over_the_xcds():
+    assert bench.mean_engine_clock([_gpu([2392, 2377, 2400, 2359, 2394, 2374, 2396, 2366])]) == \
+        pytest.approx(19058 / 8 / 1e3, abs=1e-12)
+
+
+@pytest.mark.parametrize("data", [
+    [],                                            # no GPU reported
+    None,
+    [_gpu([2400] * 8), _gpu([2400] * 8)],          # which one is ours is unknown
+    [_gpu([2392, 95, 2400, 2359, 2394, 2374, 2396, 2366])],  # one XCD asleep: an idle sample
+    [{"gpu": 0, "clock": {}}],
+])
+def test_engine_clock_rejects_readings_it_cannot_trust(data):
+    assert bench.mean_engine_clock(data) is None
