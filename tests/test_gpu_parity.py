@@ -644,3 +644,25 @@ def test_non_default_stream():
     tg.sgemm(dA, dB, out=C2, stream=s.cuda_stream)
     s.synchronize()
     assert torch.equal(C, C2)
+
+
+def test_concurrent_products_on_two_streams():
+    """Two products queued at once on two streams, each with more tiles than
+    the chip holds (so each launches the persistent grid that can fill every
+    compute unit), interleaved several times: every result exact."""
+    shapes = [(4100, 2052, 100), (2100, 4100, 68)]
+    ins = [int_inputs(M, N, K, 77 + i) for i, (M, N, K) in enumerate(shapes)]
+    want = [oracle.gemm_i64(A, B) for A, B in ins]
+    dins = [(dev(A), dev(B)) for A, B in ins]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(3)] for M, N, _ in shapes]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, s in enumerate(streams):
+            tg.sgemm(*dins[i], out=outs[i][rep], stream=s.cuda_stream)
+    for s in streams:
+        s.synchronize()
+    for i in range(2):
+        for rep in range(3):
+            log(f"concurrent stream {i} call {rep}")
+            assert_exact(outs[i][rep].cpu().numpy(), want[i], f"stream {i} call {rep}")
