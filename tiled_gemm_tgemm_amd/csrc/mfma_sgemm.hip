@@ -269,9 +269,11 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
     const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     // the grid holds at most as many work-groups as the chip holds at once;
     // each one takes tiles blockIdx.x, blockIdx.x + gridDim.x, ...
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    // (a 64-bit tile index, so that tile + gridDim.x cannot wrap for any
+    // tile count below 2^31)
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         int tm, tn;
-        mfma::tile_of(tiles_m, tiles_n, G::GROUP_M, tm, tn, tile, ntiles);
+        mfma::tile_of(tiles_m, tiles_n, G::GROUP_M, tm, tn, (int)tile, ntiles);
         const int m0 = tm * G::BM, n0 = tn * G::BN;
         const int rows_valid = min(G::BM, M - m0), cols_valid = min(G::BN, N - n0);
 
@@ -481,7 +483,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         }
         // the next tile's first write into LDS waits until every wavefront
         // is done reading this tile's last stage
-        if (tile + (int)gridDim.x < ntiles) __syncthreads();
+        if (tile + gridDim.x < ntiles) __syncthreads();
     }
 }
 
