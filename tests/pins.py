@@ -226,6 +226,37 @@ def pin_window(lib):
     return None
 
 
+def pin_leading_dimensions(lib):
+    """The C entry points with A and B embedded in wider row-major buffers
+    (lda > K, ldb > N, the padding NaN) give, bit for bit, the products of
+    the contiguous operands: the row stride is honoured and nothing outside
+    the operands is read."""
+    lib = lib or oracle._load()
+    M, K, N = 9, 13, 11
+    A = seeded((M, K), "int", 33)
+    B = seeded((K, N), "int", 34)
+    lda, ldb = K + 3, N + 5
+    Aw = np.full((M, lda), np.nan, np.float32)
+    Bw = np.full((K, ldb), np.nan, np.float32)
+    Aw[:, :K] = A
+    Bw[:, :N] = B
+    P, S = oracle.gemm(A, B, lib=lib)
+    Pw = np.empty((M, N), np.float64)
+    Sw = np.empty((M, N), np.float64)
+    rc = lib.oracle_gemm_f64_window(M, N, K, Aw, lda, Bw, ldb, 0, M, 0, N, Pw, N, Sw.ctypes.data, N)
+    if rc != 0 or not np.array_equal(Pw, P) or not np.array_equal(Sw, S):
+        return "float64 product with lda > K, ldb > N differs from the contiguous one"
+    Iw = np.empty((M, N), np.int64)
+    rc = lib.oracle_gemm_i64(M, N, K, Aw, lda, Bw, ldb, Iw, N)
+    if rc != 0 or not np.array_equal(Iw, oracle.gemm_i64(A, B, lib=lib)):
+        return "int64 product with lda > K, ldb > N differs from the contiguous one"
+    Fw = np.empty((M, N), np.float32)
+    rc = lib.oracle_gemm_fma_f32(M, N, K, Aw, lda, Bw, ldb, Fw, N)
+    if rc != 0 or not np.array_equal(Fw, oracle.gemm_fma_f32(A, B, lib=lib)):
+        return "float32 model with lda > K, ldb > N differs from the contiguous one"
+    return None
+
+
 def pin_fma_model(lib):
     """The float32 model equals step-by-step exact rounding (IEEE RNE) of a·b + acc."""
     for dist, (M, N, K) in [("uniform", (3, 4, 9)), ("wide", (4, 3, 7)), ("normal", (2, 2, 16))]:
@@ -368,7 +399,8 @@ def pin_transpose_strides(lib):
 
 
 ALL_PINS = [pin_bruteforce_rational, pin_integer_paths, pin_identities, pin_one_hot,
-            pin_transpose, pin_closed_forms, pin_worked_example, pin_window, pin_fma_model,
+            pin_transpose, pin_closed_forms, pin_worked_example, pin_window, pin_leading_dimensions,
+            pin_fma_model,
             pin_checksums, pin_empty, pin_transpose_golden, pin_transpose_closed_form,
             pin_transpose_library_and_bits, pin_transpose_strides]
 

@@ -1,9 +1,10 @@
 """Plant one plausible mistake at a time in a copy of oracle.c (on the CPU)
 and check that at least one pin catches it.  This is how the pins show they
 are strong enough: a dropped term, a wrong sign, a transposed operand, a
-wrong index, a missing absolute value, an unfused step, a wrong checksum
-weight, or a transpose that drops a column, ignores a leading dimension or
-mirrors its output must each fail something."""
+wrong index, a leading dimension ignored, a missing absolute value, an
+unfused or reordered step, a wrong checksum weight, or a transpose that
+drops a column, ignores a leading dimension or mirrors its output must each
+fail something."""
 
 import os
 import shutil
@@ -35,6 +36,15 @@ MUTANTS = {
     "transpose_ignores_ldb": ("B[j * ldb + i] = A[i * lda + j];", "B[j * M + i] = A[i * lda + j];"),
     "transpose_mirrored": ("B[j * ldb + i] = A[i * lda + j];", "B[j * ldb + (M - 1 - i)] = A[i * lda + j];"),
     "first_row_skipped": ("for (int64_t i = i0; i < i1; ++i) {", "for (int64_t i = i0 + (i1 > i0 + 1); i < i1; ++i) {"),
+    "a_ignores_lda": ("const double a = (double)A[i * lda + k];\n            const float *brow",
+                      "const double a = (double)A[i * K + k];\n            const float *brow"),
+    "b_ignores_ldb": ("const float *brow = B + k * ldb + j0;", "const float *brow = B + k * N + j0;"),
+    "k_starts_at_one": ("for (int64_t k = 0; k < K; ++k) {\n            const double a = (double)A[i * lda + k];\n            const float *brow",
+                        "for (int64_t k = (K > 1); k < K; ++k) {\n            const double a = (double)A[i * lda + k];\n            const float *brow"),
+    "int_path_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n                acc += (int64_t)",
+                              "for (int64_t k = 0; k < K - 1; ++k)\n                acc += (int64_t)"),
+    "fma_descending_k": ("for (int64_t k = 0; k < K; ++k)\n                acc = fmaf(",
+                         "for (int64_t k = K - 1; k >= 0; --k)\n                acc = fmaf("),
 }
 
 
