@@ -254,6 +254,11 @@ def pin_leading_dimensions(lib):
     rc = lib.oracle_gemm_fma_f32(M, N, K, Aw, lda, Bw, ldb, Fw, N)
     if rc != 0 or not np.array_equal(Fw, oracle.gemm_fma_f32(A, B, lib=lib)):
         return "float32 model with lda > K, ldb > N differs from the contiguous one"
+    want = oracle.checksums(A, B, lib=lib)
+    got = [np.empty(M), np.empty(M), np.empty(N), np.empty(N)]
+    rc = lib.oracle_checksums(M, N, K, Aw, lda, Bw, ldb, *got, np.empty(4 * K))
+    if rc != 0 or not all(np.array_equal(g, w) for g, w in zip(got, want)):
+        return "checksums with lda > K, ldb > N differ from the contiguous ones"
     return None
 
 

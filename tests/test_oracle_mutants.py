@@ -43,6 +43,8 @@ MUTANTS = {
                         "for (int64_t k = (K > 1); k < K; ++k) {\n            const double a = (double)A[i * lda + k];\n            const float *brow"),
     "int_path_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n                acc += (int64_t)",
                               "for (int64_t k = 0; k < K - 1; ++k)\n                acc += (int64_t)"),
+    "checksums_ignore_lda": ("s += (double)A[i * lda + k];\n            sa += fabs((double)A[i * lda + k]);",
+                             "s += (double)A[i * K + k];\n            sa += fabs((double)A[i * K + k]);"),
     "fma_descending_k": ("for (int64_t k = 0; k < K; ++k)\n                acc = fmaf(",
                          "for (int64_t k = K - 1; k >= 0; --k)\n                acc = fmaf("),
 }
