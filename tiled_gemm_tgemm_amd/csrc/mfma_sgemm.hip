@@ -5,8 +5,8 @@
 // follows the tiling plan of page 1's section [Shared Memory] and page 2
 // ("Lec 29 · GPU Architecture (2)") §1.1-1.2, redone for CDNA4:
 //
-// * One work-group owns a BM×BN tile of C and walks K in phases of BK
-//   (page 1, "Work Flow - Compute Block(0, 0)": tile phases).
+// * A work-group computes one BM×BN tile of C at a time and walks K in
+//   phases of BK (page 1, "Work Flow - Compute Block(0, 0)": tile phases).
 // * Per phase the work-group copies a BM×BK slice of A and a BK×BN slice of B
 //   from device memory into LDS.  Consecutive lanes read consecutive
 //   addresses of one row (page 1, section [Coalescing]; page 2 §1.4, bursts):
@@ -44,6 +44,8 @@
 //   to arrive, so a miss in L2 rarely stalls the LDS write.  The two register
 //   sets alternate, so the main loop is unrolled by two and has no branches;
 //   the last phases (the partial K phase among them) run in a tail loop.
+//   (The 256×128 configuration with 4-byte loads has one register set: its
+//   loads run two phases ahead, see below.)
 //   Measured on MI355X at 8192³ (4096³), bit-identical results, by how many
 //   phases ahead of its computation a phase's loads are issued (before the
 //   lean loads and the persistent grid): one (the next phase only, issued
