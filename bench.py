@@ -126,6 +126,9 @@ def parse():
                    help="T: A is stored transposed (K×M) and passed as TGEMM_OP_T")
     p.add_argument("--op-b", choices=("N", "T"), default="N",
                    help="T: B is stored transposed (N×K) and passed as TGEMM_OP_T")
+    p.add_argument("--no-engine-clock", action="store_true",
+                   help="skip the amd-smi clock reading (a child process); use it under a profiler "
+                        "that loads itself into every child")
     p.add_argument("--cold", action="store_true",
                    help="before every timed call, overwrite a 512 MiB buffer so that L2 and the "
                         "256 MB Infinity Cache hold none of the operands (kernel time only)")
@@ -635,7 +638,7 @@ def main():
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "hip": torch.version.hip},
     }
-    if not args.cold:
+    if not args.cold and not args.no_engine_clock:
         ghz = engine_clock(m, args.kernel)
         # flops per clock and CU: 256 on the fp32 matrix cores, 128 as unpacked vector FMAs
         per_clk = 256 if bound == "mfma" else 128

@@ -151,7 +151,7 @@ def test_transposed_variant_choice(lib):
 
     assert chosen(T_, N_, 4096, 4096, 4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
     assert chosen(N_, T_, 8192, 8192, 8192, 8192, 8192) == "m256n128k16_w2x2_vec4"
-    assert chosen(T_, T_, 512, 512, 512, 512, 512) == "m32n32k8_s4d4_vec4"
+    assert chosen(T_, T_, 512, 512, 512, 512, 512) == "m32n32k32_w1x1s8_vec4"
     # Aᵀ with M not a multiple of 4: its stored rows cannot take 16-byte loads
     assert chosen(T_, N_, 4098, 4096, 4096, 4098, 4096).endswith("vec1")
     # row-major A with K not a multiple of 4, but Aᵀ rows (length M) can
@@ -197,13 +197,18 @@ def test_variant_choice(lib):
     assert chosen(8192, 8192, 8192) == "m256n128k16_w2x2_vec4"
     assert chosen(4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
     assert chosen(3000, 5000, 1000) == "m256n128k16_w2x2_vec4"
-    assert chosen(512, 512, 512) == "m32n32k8_s4d4_vec4"      # split-K small-product kernel
+    # 32×32 tiles with K split over eight wavefronts: 7.5 µs against 10.3 for
+    # the small-product kernel and 11.7 for 64×64 tiles on MI355X
+    assert chosen(512, 512, 512) == "m32n32k32_w1x1s8_vec4"
     assert chosen(1024, 1024, 1024) == "m64n64k32_w2x2_vec4"
     assert chosen(2048, 2048, 2048) == "m128n128k32_w2x2_vec4"  # 123.6 µs vs 127.6 for 64×64
-    assert chosen(640, 640, 640) == "m64n64k32_w2x2_vec4"       # 15.2 µs vs 23.1 split-K on MI355X
+    assert chosen(640, 640, 640) == "m32n32k32_w1x1s4_vec4"     # 11.1 µs vs 13.6 for 64×64 on MI355X
     assert chosen(2500, 2500, 2500) == "m64n64k32_w2x2_vec4"    # 272 µs vs 305 for 128×128
     assert chosen(6144, 6144, 6144) == "m128n128k32_w2x2_vec4"
-    assert chosen(256, 256, 8192) == "m32n32k8_s8d8_vec4"
+    assert chosen(256, 256, 8192) == "m32n32k32_w1x1s8_vec4"    # 50.0 µs vs 80.5 small-product kernel
+    assert chosen(2048, 256, 8192) == "m32n32k32_w1x1s4_vec4"   # 92.0 µs vs 131.2 for 64×64
+    assert chosen(2048, 256, 8192, a=(1 << 40) + 4) == "m32n32k32_w1x1s4_vec1"  # 153 µs vs 263 small-product
+    assert chosen(64, 64, 64) == "m64n64k32_w2x2_vec4"          # 4.0 µs vs 5.0 for 32×32 tiles
     # long K on few tiles: the unsplit 64×64 tile (133 µs on MI355X) ahead of
     # the four-way K split inside the work-group (148 µs)
     assert chosen(1024, 1024, 8192) == "m64n64k32_w2x2_vec4"

@@ -72,7 +72,8 @@
 //   8192³ with 4-byte loads forced: plain schedule 140.3 TFLOP/s,
 //   interleaved with one set 148.8, with two sets 134.3 (spilling); at
 //   128×128 two sets are ahead (139.3 against 133.3 plain).
-// * K split inside a work-group (the 64×64 configurations with KS = 2 or 4):
+// * K split inside a work-group (64×64 tiles with KS = 2 or 4 groups of four
+//   wavefronts; 32×32 tiles with KS = 4 or 8 single wavefronts):
 //   on shapes with too few tiles to give every SIMD more than one wavefront
 //   (about 1024³, or small M·N with long K), the work-group holds KS groups
 //   of wavefronts, each running the pipeline above over its own slice of K
@@ -85,7 +86,11 @@
 //   the whole-phase loads and the persistent grid, the unsplit 64×64 tile is
 //   ahead on every shape measured (1024×1024×8192: 133 against 148 µs;
 //   768×768×8192: 132 against 147 µs), so the selection model no longer
-//   picks these; they stay available through tgemm_sgemm_mfma.
+//   picks the 64×64 splits; they stay available through tgemm_sgemm_mfma.
+//   With 32×32 tiles and one wavefront per slice the split is what fills
+//   the chip where even 64×64 tiles leave CUs idle (512³: 7.5 µs against
+//   10.3 for the small-product kernel; 512×512×16384: 94.8 against 156;
+//   2048×256×8192: 92.0 against 131 for 64×64).
 // * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
@@ -552,10 +557,10 @@ constexpr int64_t max_ld()
 
 // One tile shape (with KS slices of K per work-group) in its four operand
 // orders (NN, TN, NT, TT).
-template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1, int NS = 2>
+template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1, int NS = 2, int W = 2>
 struct Shape {
     template <bool TA, bool TB>
-    using C = Cfg<BM, BN, BK, 2, 2, VEC, GM, OCC, TA, TB, KS, NS>;
+    using C = Cfg<BM, BN, BK, W, W, VEC, GM, OCC, TA, TB, KS, NS>;
     static hipError_t launch(const GemmArgs &g, hipStream_t stream)
     {
         switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
@@ -578,11 +583,16 @@ typedef Shape<64, 64, 32, 4, 8, 4, 2> Small4x2;  // K split over two groups of w
 typedef Shape<64, 64, 32, 4, 8, 4, 4> Small4x4;  // ... over four
 typedef Shape<64, 64, 32, 1, 8, 4, 2> Small1x2;
 typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
+typedef Shape<32, 32, 32, 4, 8, 4, 4, 2, 1> Tiny4x4;  // one wavefront per K slice
+typedef Shape<32, 32, 32, 4, 8, 2, 8, 2, 1> Tiny4x8;
+typedef Shape<32, 32, 32, 1, 8, 4, 4, 2, 1> Tiny1x4;
+typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 
 #define TGEMM_VARIANT(name, S, alone, full, round)                                                  \
     {                                                                                                \
         name, S::template C<false, false>::BM, S::template C<false, false>::BN,                     \
-            S::template C<false, false>::BK, S::template C<false, false>::VEC,                      \
+            S::template C<false, false>::BK * S::template C<false, false>::KS,                      \
+            S::template C<false, false>::VEC,                                                       \
             wg_per_cu<typename S::template C<false, false>>(),                                      \
             max_ld<typename S::template C<false, false>::LA>(),                                     \
             max_ld<typename S::template C<false, false>::LB>(),                                     \
@@ -605,7 +615,12 @@ typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
 // efficiency alone was raised to match; a sweep of 20 shapes from 128³ to
 // 6144³ (square, ragged, long and short K) then finds the model's pick the
 // fastest or within 2% of it, apart from 128³ (5.5 µs against 5.1 µs).  The 4-byte-load flavours keep the
-// measured ratio to the 16-byte ones.
+// measured ratio to the 16-byte ones.  The 32×32 K-split configurations were
+// fitted to a sweep of 27 small, ragged, skinny and long-K shapes with both
+// load widths (one work-group per CU: 256 tiles with K = 16384; CU full: 512
+// tiles with K = 4096 and 8192; the fixed cost from 256³ and 512³), after
+// which every pick on that sweep is the fastest or within 3% of it, apart
+// from 300³ with 4-byte loads (4%).
 const MfmaVariant kVariants[] = {
     TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.97, 0.97, 7000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.96, 0.96, 7000.0),
@@ -617,6 +632,10 @@ const MfmaVariant kVariants[] = {
     TGEMM_VARIANT("m64n64k32_w2x2s4_vec4", Small4x4, 0.72, 0.72, 10000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s2_vec1", Small1x2, 0.44, 0.55, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s4_vec1", Small1x4, 0.55, 0.55, 10000.0),
+    TGEMM_VARIANT("m32n32k32_w1x1s4_vec4", Tiny4x4, 0.46, 0.62, 9500.0),
+    TGEMM_VARIANT("m32n32k32_w1x1s8_vec4", Tiny4x8, 0.60, 0.60, 11500.0),
+    TGEMM_VARIANT("m32n32k32_w1x1s4_vec1", Tiny1x4, 0.24, 0.37, 12000.0),
+    TGEMM_VARIANT("m32n32k32_w1x1s8_vec1", Tiny1x8, 0.36, 0.36, 15000.0),
 };
 
 }  // namespace

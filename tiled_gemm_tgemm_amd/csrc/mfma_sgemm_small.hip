@@ -210,18 +210,20 @@ constexpr int64_t kMaxLdKc = ((((int64_t)1 << 31) - 16) / 4 - 8) / 32;
 constexpr int64_t kMaxLdMc = ((((int64_t)1 << 31) - 16) / 4 - 32) / 8;
 
 // bk = 8·KS: the K granularity of a work-group.  Efficiencies and the fixed
-// cost per round fitted (least squares on log time) to the times measured on
-// MI355X over 23 shapes from 128³ to 8192³ (ragged and long-K ones among
-// them); the 4-byte-load flavours keep the ratio to the 16-byte ones
-// measured earlier (about 0.8).
+// cost per round measured on MI355X over 27 small, ragged, skinny and long-K
+// shapes with both load widths (one work-group per CU: 256 tiles with
+// K = 16384; CU full: 512 or 1024 tiles; the fixed cost from 64³).  On every
+// one of them a 32×32 tile of the LDS-staged kernel with K split over its
+// wavefronts (mfma_sgemm.hip) is as fast or faster, so the selection model
+// does not pick these; they stay available through tgemm_sgemm_mfma.
 const MfmaVariant kSmallVariants[] = {
-    {"m32n32k8_s4d4_vec4", 32, 32, 32, 4, 4, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.24, 0.46, 7000.0,
+    {"m32n32k8_s4d4_vec4", 32, 32, 32, 4, 4, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.24, 0.39, 10000.0,
      &S4D4v4::launch},
-    {"m32n32k8_s8d8_vec4", 32, 32, 64, 4, 2, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.40, 0.48, 18000.0,
+    {"m32n32k8_s8d8_vec4", 32, 32, 64, 4, 2, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.365, 0.43, 22000.0,
      &S8D8v4::launch},
-    {"m32n32k8_s4d4_vec1", 32, 32, 32, 1, 4, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.19, 0.37, 7000.0,
+    {"m32n32k8_s4d4_vec1", 32, 32, 32, 1, 4, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.18, 0.20, 10000.0,
      &S4D4v1::launch},
-    {"m32n32k8_s8d8_vec1", 32, 32, 64, 1, 2, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.32, 0.38, 18000.0,
+    {"m32n32k8_s8d8_vec1", 32, 32, 64, 1, 2, kMaxLdKc, kMaxLdMc, kMaxLdMc, kMaxLdKc, true, 0.215, 0.21, 22000.0,
      &S8D8v1::launch},
 };
 

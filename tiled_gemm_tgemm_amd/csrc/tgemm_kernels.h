@@ -53,7 +53,7 @@ hipError_t launch_transpose(TransposeKind kind, const TransposeArgs &t, hipStrea
 // Matrix-core tile configurations.
 struct MfmaVariant {
     const char *name;
-    int bm, bn, bk;      // macro tile and phase depth
+    int bm, bn, bk;      // macro tile; K granularity of a work-group (phase depth × K slices)
     int vec;             // 4: 16-byte loads (alignment required), 1: 4-byte loads
     int wg_per_cu;       // work-groups one compute unit holds at once
     int64_t max_lda;     // largest leading dimensions the configuration takes,
