@@ -44,6 +44,7 @@
 #ifndef TGEMM_H
 #define TGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -97,6 +98,41 @@ tgemm_status_t tgemm_sgemm_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64
                               const float *A, int64_t lda,
                               const float *B, int64_t ldb,
                               float *C, int64_t ldc, hipStream_t stream);
+
+/*
+ * C = A·B (row-major operands, as tgemm_sgemm) with the k range split
+ * across work-groups: the sum over k of page 1's section [Matrix
+ * Multiplication] taken in up to `splits` contiguous slices that run side by
+ * side, each slice's partial product written to its own M×N block of
+ * `workspace`, and a second pass adding the blocks into C in slice order.
+ * For shapes with too few output tiles to fill the GPU and a long K (e.g.
+ * 512×512×16384).  Results do not depend on timing; the summation order
+ * differs from tgemm_sgemm's, within the same error bound, and integer
+ * inputs whose sums stay below 2^24 give the same exact results.
+ *   splits: 1 ... 64; 1 runs tgemm_sgemm (workspace unused, may be NULL).
+ *     The library may run fewer slices than asked (each slice is a whole
+ *     number of its tile configuration's K steps), never more.
+ *   workspace: device memory owned by the caller, 16-byte aligned, at least
+ *     tgemm_sgemm_splitk_workspace_size(M, N, K, splits) bytes, overlapping
+ *     none of A, B, C; its contents on return are unspecified.  The call
+ *     allocates nothing.  Two calls in flight at once need two workspaces.
+ * Errors as tgemm_sgemm; also TGEMM_ERROR_INVALID_VALUE for splits outside
+ * 1 ... 64, a missing, misaligned, overlapping or too small workspace.
+ */
+tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K,
+                                  const float *A, int64_t lda,
+                                  const float *B, int64_t ldb,
+                                  float *C, int64_t ldc, int splits,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes tgemm_sgemm_splitk needs: splits·M·N·4; 0 when splits <= 1,
+ * splits > 64 or a size is not positive or above 2^31-2^16. */
+size_t tgemm_sgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits);
+
+/* The split count (1, 2, 4, ..., 64) the library's cost model expects to be
+ * fastest for M, N, K with 16-byte-aligned row-major operands; 1 means no
+ * split (then tgemm_sgemm is the call to make).  Host-only: no GPU work. */
+int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K);
 
 /*
  * Same product with an explicitly chosen matrix-core tile configuration,

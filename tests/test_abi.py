@@ -304,3 +304,42 @@ def test_host_empty_sum_is_written_on_the_host(lib):
     st = tg.tgemm_sgemm_host(3, 5, 0, 0, 1, 0, 5, C.ctypes.data, 7, 0, 0, 0, None, None, None)
     assert st == tg.TGEMM_SUCCESS
     assert np.all(C[:, :5] == 0) and not np.any(np.signbit(C[:, :5])) and np.all(np.isnan(C[:, 5:]))
+
+
+def test_splitk_workspace_size_and_choice(lib):
+    assert tg.tgemm_sgemm_splitk_workspace_size(100, 60, 1000, 4) == 4 * 100 * 60 * 4
+    assert tg.tgemm_sgemm_splitk_workspace_size(100, 60, 1000, 64) == 64 * 100 * 60 * 4
+    for bad in [(100, 60, 1000, 1), (100, 60, 1000, 0), (100, 60, 1000, -2), (100, 60, 1000, 65),
+                (0, 60, 1000, 4), (100, 0, 1000, 4), (100, 60, 0, 4), (-1, 60, 1000, 4),
+                (MAX_DIM + 1, 4, 4, 4)]:
+        assert tg.tgemm_sgemm_splitk_workspace_size(*bad) == 0, bad
+    # many tiles: no split; few tiles with long K: a split (50.0 µs at 8
+    # slices against 80.5 for the best unsplit kernel at 256×256×8192)
+    assert tg.tgemm_sgemm_splitk_choose(8192, 8192, 8192) == 1
+    assert tg.tgemm_sgemm_splitk_choose(4096, 4096, 4096) == 1
+    for shape in [(256, 256, 16384), (512, 512, 16384), (2048, 256, 8192)]:
+        s = tg.tgemm_sgemm_splitk_choose(*shape)
+        assert s in (2, 4, 8, 16, 32, 64), (shape, s)
+    assert tg.tgemm_sgemm_splitk_choose(0, 4, 4) == 1 and tg.tgemm_sgemm_splitk_choose(4, 4, -1) == 1
+
+
+def test_splitk_argument_checks(lib):
+    M, N, K = 64, 64, 4096
+    args = (M, N, K, A_, K, B_, N, C_, N)
+    W_ = 0x40000000
+    need = tg.tgemm_sgemm_splitk_workspace_size(M, N, K, 4)
+    assert need == 4 * M * N * 4
+    for splits in (0, -1, 65):
+        assert tg.tgemm_sgemm_splitk(*args, splits, W_, need, None) == INVALID
+    assert tg.tgemm_sgemm_splitk(*args, 4, None, need, None) == INVALID          # no workspace
+    assert tg.tgemm_sgemm_splitk(*args, 4, W_ + 4, need, None) == INVALID       # misaligned
+    assert tg.tgemm_sgemm_splitk(*args, 4, W_, need - 4, None) == INVALID       # too small
+    assert tg.tgemm_sgemm_splitk(*args, 4, C_, need, None) == INVALID           # overlaps C
+    assert tg.tgemm_sgemm_splitk(*args, 4, A_ + 4096, need, None) == INVALID    # overlaps A
+    assert tg.tgemm_sgemm_splitk(*args, 4, 2 ** 64 - 256, need, None) == INVALID  # wraps around
+    # the product's own checks come first
+    assert tg.tgemm_sgemm_splitk(M, N, K, A_, K - 1, B_, N, C_, N, 4, W_, need, None) == INVALID
+    assert tg.tgemm_sgemm_splitk(-1, N, K, A_, K, B_, N, C_, N, 4, W_, need, None) == INVALID
+    # empty products finish without a launch, whatever the workspace
+    assert tg.tgemm_sgemm_splitk(0, N, K, A_, K, B_, N, C_, N, 4, None, 0, None) == tg.TGEMM_SUCCESS
+    assert tg.tgemm_sgemm_splitk(M, 0, K, A_, K, B_, 1, C_, 1, 4, None, 0, None) == tg.TGEMM_SUCCESS

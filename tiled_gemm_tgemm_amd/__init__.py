@@ -37,6 +37,9 @@ from ._lib import (  # noqa: F401
     tgemm_sgemm_simt,
     tgemm_sgemm_host,
     tgemm_sgemm_host_workspace_size,
+    tgemm_sgemm_splitk,
+    tgemm_sgemm_splitk_choose,
+    tgemm_sgemm_splitk_workspace_size,
     tgemm_sgemm_variant_for,
     tgemm_status_string,
     tgemm_transpose,
@@ -117,6 +120,51 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
         raise ValueError(f"kernel must be one of {KERNELS}")
     if st != TGEMM_SUCCESS:
         raise TgemmError(st, f"tgemm ({kernel})")
+    return out
+
+
+def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
+    """C = A·B for row-major float32 CUDA tensors with K split across
+    work-groups (tgemm_sgemm_splitk), for shapes with few output tiles and a
+    long K.  splits: None for the library's choice (tgemm_sgemm_splitk_choose),
+    else 1 ... 64.  workspace: a CUDA uint8 tensor of at least
+    tgemm_sgemm_splitk_workspace_size bytes (allocated if omitted; two calls
+    in flight at once need two).  Queued on `stream` (default: torch's current
+    stream); returns `out` without waiting."""
+    import torch
+
+    A = _check(A, "A")
+    B = _check(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    op_a, lda = _layout(A, "A")
+    op_b, ldb = _layout(B, "B")
+    if (op_a, op_b) != (TGEMM_OP_N, TGEMM_OP_N):
+        raise ValueError("sgemm_splitk takes row-major operands only")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        out = _check(out, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be {M}x{N}")
+        if out.stride(1) != 1 and N > 1:
+            raise ValueError("out must be row-major")
+    ldc = max(out.stride(0), N, 1)
+    if splits is None:
+        splits = tgemm_sgemm_splitk_choose(M, N, K)
+    need = tgemm_sgemm_splitk_workspace_size(M, N, K, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A.device)
+    elif not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a CUDA uint8 tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    st = tgemm_sgemm_splitk(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, splits,
+                            workspace.data_ptr(), workspace.numel(), stream)
+    if st != TGEMM_SUCCESS:
+        raise TgemmError(st, "tgemm_sgemm_splitk")
     return out
 
 

@@ -25,7 +25,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtgemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "host_pipeline.cpp", "naive.hip", "lds_tiled.hip", "simt_tiled.hip", "transpose.hip",
+SOURCES = ["api.cpp", "host_pipeline.cpp", "naive.hip", "lds_tiled.hip", "simt_tiled.hip", "transpose.hip", "splitk_sum.hip",
            "mfma_sgemm.hip", "mfma_sgemm_small.hip", "mfma_sgemm_flat.hip"]
 
 ARCH = "gfx950"

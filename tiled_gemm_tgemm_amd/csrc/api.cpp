@@ -109,10 +109,9 @@ bool runs(const tgemm::MfmaVariant &v, bool vec4, bool ta, bool tb, int64_t lda,
 // leave CUs less full, and is costed at its own residency.  Edge tiles cost
 // as much as full ones, which is what makes smaller tiles win on small or
 // ragged shapes.
-double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
+double cost_tiles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t K)
 {
     const int64_t cus = 256;
-    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
     const int64_t full_rounds = tiles / (cus * v.wg_per_cu);
     const int64_t rest = tiles % (cus * v.wg_per_cu);
     const double kpad = (double)((K + v.bk - 1) / v.bk) * v.bk;
@@ -128,6 +127,59 @@ double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
     }
     return t;
 }
+
+double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
+{
+    return cost_tiles(v, ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn), K);
+}
+
+// K split across work-groups.  Slices are a whole number of a configuration's
+// K granularity (phase depth × K slices inside the work-group) long, so only
+// the last slice has a partial phase, and a multiple of 4, so 16-byte loads
+// stay aligned; `splits` is an upper bound on the slices actually run.
+struct Split {
+    int variant = -1;
+    int slices = 1;
+    int kchunk = 0;
+    double cycles = 0;
+};
+
+int64_t kchunk_for(const tgemm::MfmaVariant &v, int64_t K, int splits)
+{
+    const int64_t per = (K + splits - 1) / splits;
+    return (per + v.bk - 1) / v.bk * v.bk;
+}
+
+// The second pass reads S slices of M×N floats and writes C once; costed at
+// 5 TB/s (a plain streaming copy on MI355X reaches 5.4-5.6) plus a launch.
+double sum_cycles(int64_t M, int64_t N, int slices)
+{
+    return (double)(slices + 1) * M * N * 4.0 / 5.0e12 * 2.4e9 + 7000.0;
+}
+
+// Best configuration for exactly up to `splits` slices (splits >= 2).
+Split choose_split(int64_t M, int64_t N, int64_t K, bool vec4, int64_t lda, int64_t ldb, int splits)
+{
+    Split best;
+    for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
+        const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
+        if (!v->split_k || !runs(*v, vec4, false, false, lda, ldb)) continue;
+        const int64_t kc = kchunk_for(*v, K, splits);
+        const int64_t slices = (K + kc - 1) / kc;
+        const int64_t tiles = ((M + v->bm - 1) / v->bm) * ((N + v->bn - 1) / v->bn);
+        const double c = cost_tiles(*v, tiles * slices, kc) + (slices > 1 ? sum_cycles(M, N, (int)slices) : 0.0);
+        if (best.variant < 0 || c < best.cycles) {
+            best.variant = i;
+            best.slices = (int)slices;
+            best.kchunk = (int)kc;
+            best.cycles = c;
+        }
+    }
+    return best;
+}
+
+constexpr int kMaxSplits = 64;
+constexpr int64_t kMinSliceK = 1024;
 
 int choose_variant(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                    const float *B, int64_t ldb)
@@ -194,6 +246,75 @@ tgemm_status_t tgemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int6
                            const float *B, int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
 {
     return tgemm_sgemm_ex(TGEMM_OP_N, TGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+size_t tgemm_sgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || splits <= 1 || splits > kMaxSplits) return 0;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 1;
+    // row-major operands with 16-byte loads, as tgemm_sgemm would run them
+    double best = -1;
+    for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
+        const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
+        if (!runs(*v, true, false, false, max1(K), max1(N))) continue;
+        const double c = cost(*v, M, N, K);
+        if (best < 0 || c < best) best = c;
+    }
+    // slices shorter than ~1024 values of k lose more to each work-group's
+    // pipeline fill and drain than they gain (measured on MI355X: at
+    // 384×640×4096, 23.7 µs with 4 slices against 30.4 with 16)
+    int pick = 1;
+    for (int splits = 2; splits <= kMaxSplits && (K + splits - 1) / splits >= kMinSliceK; splits *= 2) {
+        const Split sp = choose_split(M, N, K, true, max1(K), max1(N), splits);
+        if (sp.variant >= 0 && sp.slices > 1 && (best < 0 || sp.cycles < best)) {
+            best = sp.cycles;
+            pick = splits;
+        }
+    }
+    return pick;
+}
+
+tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                                  const float *B, int64_t ldb, float *C, int64_t ldc, int splits,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    Quick quick;
+    const tgemm_status_t st = validate(false, false, M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS) return st;
+    if (splits < 1 || splits > kMaxSplits) return TGEMM_ERROR_INVALID_VALUE;
+    if (quick == Quick::kDone) return TGEMM_SUCCESS;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if (splits == 1) return tgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream);
+    // the workspace: `splits` blocks of M×N floats, 16-byte aligned, apart from A, B and C
+    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 ||
+        workspace_bytes < tgemm_sgemm_splitk_workspace_size(M, N, K, splits))
+        return TGEMM_ERROR_INVALID_VALUE;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
+    if (workspace_bytes > UINTPTR_MAX - w0) return TGEMM_ERROR_INVALID_VALUE;
+    const uintptr_t w1 = w0 + workspace_bytes;
+    uintptr_t x0, x1;
+    if (span(A, M, K, lda, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    if (span(B, K, N, ldb, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    if (span(C, M, N, ldc, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    const bool vec4 = vec4_ok(false, false, M, N, K, A, lda, B, ldb);
+    const Split sp = choose_split(M, N, K, vec4, lda, ldb, splits);
+    if (sp.variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
+    if (sp.slices <= 1) return tgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream);
+    float *W = static_cast<float *>(workspace);
+    GemmArgs g = pack(false, false, M, N, K, A, lda, B, ldb, W, N);
+    g.splits = sp.slices;
+    g.kchunk = sp.kchunk;
+    g.c_slice = M * N;
+    const tgemm::MfmaVariant *v = tgemm::mfma_variant(sp.variant);
+    const hipError_t e = v->launch(g, stream);
+    if (e != hipSuccess) return TGEMM_ERROR_HIP;
+    return from_hip(tgemm::launch_splitk_sum((int)M, (int)N, sp.slices, W, C, ldc, stream));
 }
 
 int tgemm_mfma_variant_count(void) { return tgemm::mfma_variant_count(); }

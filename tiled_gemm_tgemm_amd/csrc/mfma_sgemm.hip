@@ -91,6 +91,11 @@
 //   the chip where even 64×64 tiles leave CUs idle (512³: 7.5 µs against
 //   10.3 for the small-product kernel; 512×512×16384: 94.8 against 156;
 //   2048×256×8192: 92.0 against 131 for 64×64).
+// * K split across work-groups (gridDim.y > 1, from tgemm_sgemm_splitk):
+//   work-group (x, s) runs the whole pipeline above over the k range
+//   [s·kchunk, min(K, (s+1)·kchunk)) and writes its partial tiles to block s
+//   of a workspace; splitk_sum.hip adds the blocks in slice order.  The grid
+//   is then one work-group per tile and slice.
 // * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
@@ -263,10 +268,20 @@ template <class G>
 __global__ __launch_bounds__(G::NT) __attribute__((amdgpu_waves_per_eu(G::OCC, G::OCC)))
 void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t lda,
                        const float *__restrict__ B, int64_t ldb, float *__restrict__ C,
-                       int64_t ldc)
+                       int64_t ldc, int kchunk, int64_t c_slice)
 {
     typedef typename G::LA LA;
     typedef typename G::LB LB;
+
+    if (gridDim.y > 1) {
+        // K split across work-groups: slice blockIdx.y is the product over
+        // its own kchunk values of k, written to its own block of C
+        const int kb = (int)blockIdx.y * kchunk;
+        A += LA::KC ? (int64_t)kb : (int64_t)kb * lda;
+        B += LB::KC ? (int64_t)kb : (int64_t)kb * ldb;
+        K = min(kchunk, K - kb);
+        C += (int64_t)blockIdx.y * c_slice;
+    }
 
     __shared__ __attribute__((aligned(16))) float lds[G::LDS_WORDS];
 
@@ -532,18 +547,26 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream)
 {
     const int64_t tiles = (int64_t)((g.M + G::BM - 1) / G::BM) * ((g.N + G::BN - 1) / G::BN);
     if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // every slice holds at least one value of k
+    if (g.splits < 1 || g.splits > 65535 || (g.splits > 1 && (g.kchunk < 1 || (int64_t)(g.splits - 1) * g.kchunk >= g.K)))
+        return hipErrorInvalidValue;
+    // with K split across work-groups the grid is one work-group per tile
+    // and slice: a persistent grid per slice would hand the tiles left over
+    // after its first round to work-groups with the same blockIdx.x in every
+    // slice, which the hardware places on the same few CUs (768×768×8192 in
+    // eight slices: 130 µs against ~85 one work-group per tile)
     int64_t grid = tiles;
     if constexpr (G::KS == 1) {
         const int64_t slots = (int64_t)compute_units() * wg_per_cu<G>();
-        if (slots > 0 && slots < tiles) grid = slots;
+        if (g.splits == 1 && slots > 0 && slots < tiles) grid = slots;
     }
-    int M = g.M, N = g.N, K = g.K;
+    int M = g.M, N = g.N, K = g.K, kchunk = g.kchunk;
     const float *A = g.A, *B = g.B;
     float *C = g.C;
-    int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
-    void *args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc};
+    int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc, c_slice = g.c_slice;
+    void *args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &C, &ldc, &kchunk, &c_slice};
     return hipLaunchKernel(reinterpret_cast<const void *>(&mfma_sgemm_kernel<G>),
-                           dim3((unsigned)grid), dim3(G::NT), args, 0, stream);
+                           dim3((unsigned)grid, (unsigned)g.splits), dim3(G::NT), args, 0, stream);
 }
 
 // Buffer offsets are 32-bit and kept below 2^31: a slot's offset spans at
@@ -583,9 +606,9 @@ typedef Shape<64, 64, 32, 4, 8, 4, 2> Small4x2;  // K split over two groups of w
 typedef Shape<64, 64, 32, 4, 8, 4, 4> Small4x4;  // ... over four
 typedef Shape<64, 64, 32, 1, 8, 4, 2> Small1x2;
 typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
-typedef Shape<32, 32, 32, 4, 8, 4, 4, 2, 1> Tiny4x4;  // one wavefront per K slice
+typedef Shape<32, 32, 32, 4, 8, 2, 4, 2, 1> Tiny4x4;  // one wavefront per K slice
 typedef Shape<32, 32, 32, 4, 8, 2, 8, 2, 1> Tiny4x8;
-typedef Shape<32, 32, 32, 1, 8, 4, 4, 2, 1> Tiny1x4;
+typedef Shape<32, 32, 32, 1, 8, 2, 4, 2, 1> Tiny1x4;
 typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 
 #define TGEMM_VARIANT(name, S, alone, full, round)                                                  \
@@ -597,7 +620,8 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
             max_ld<typename S::template C<false, false>::LA>(),                                     \
             max_ld<typename S::template C<false, false>::LB>(),                                     \
             max_ld<typename S::template C<true, false>::LA>(),                                      \
-            max_ld<typename S::template C<false, true>::LB>(), true, alone, full, round, &S::launch  \
+            max_ld<typename S::template C<false, true>::LB>(), true, alone, full, round, &S::launch, \
+            true                                                                                     \
     }
 
 // Efficiencies measured on MI355X: 256 tiles with K = 8192 (one work-group per
@@ -632,7 +656,7 @@ const MfmaVariant kVariants[] = {
     TGEMM_VARIANT("m64n64k32_w2x2s4_vec4", Small4x4, 0.72, 0.72, 10000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s2_vec1", Small1x2, 0.44, 0.55, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2s4_vec1", Small1x4, 0.55, 0.55, 10000.0),
-    TGEMM_VARIANT("m32n32k32_w1x1s4_vec4", Tiny4x4, 0.46, 0.62, 9500.0),
+    TGEMM_VARIANT("m32n32k32_w1x1s4_vec4", Tiny4x4, 0.45, 0.61, 9500.0),
     TGEMM_VARIANT("m32n32k32_w1x1s8_vec4", Tiny4x8, 0.60, 0.60, 11500.0),
     TGEMM_VARIANT("m32n32k32_w1x1s4_vec1", Tiny1x4, 0.24, 0.37, 12000.0),
     TGEMM_VARIANT("m32n32k32_w1x1s8_vec1", Tiny1x8, 0.36, 0.36, 15000.0),

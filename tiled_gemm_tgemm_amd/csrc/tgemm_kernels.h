@@ -21,6 +21,12 @@ struct GemmArgs {
     float *C;
     int64_t ldc;
     bool trans_a = false, trans_b = false;
+    // K split across work-groups (tiled buffer-load kernels only): `splits`
+    // slices of `kchunk` values of k (the last one shorter); slice s reads
+    // its k range of A and B and writes its partial product to C + s·c_slice.
+    int splits = 1;
+    int kchunk = 0;
+    int64_t c_slice = 0;
 };
 
 // One thread per output, 16×16 blocks.
@@ -34,6 +40,10 @@ hipError_t launch_simt_tiled(const GemmArgs &g, hipStream_t stream);
 
 // C(i,j) = +0 for i < M, j < N (the empty sum, K = 0).
 hipError_t launch_fill_zero(int M, int N, float *C, int64_t ldc, hipStream_t stream);
+
+// C = W_0 + W_1 + ... + W_{S-1}, added in slice order (splitk_sum.hip); W_s
+// is M×N with leading dimension N at W + s·M·N.
+hipError_t launch_splitk_sum(int M, int N, int S, const float *W, float *C, int64_t ldc, hipStream_t stream);
 
 // B (N×M) = Aᵀ for A (M×N): B[j*ldb + i] = A[i*lda + j].  vec4: A and B
 // 16-byte aligned and lda, ldb multiples of 4 (16-byte accesses allowed).
@@ -67,6 +77,7 @@ struct MfmaVariant {
     // configurations for a shape.
     double eff_alone, eff_full, round_cycles;
     hipError_t (*launch)(const GemmArgs &g, hipStream_t stream);
+    bool split_k = false;  // takes GemmArgs::splits > 1
 };
 
 // Tiled buffer-load kernels (mfma_sgemm.hip), the small-product kernel
