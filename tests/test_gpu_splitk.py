@@ -167,3 +167,58 @@ def test_splitk_sampled_at_size():
     row, rowabs, col, colabs = oracle.checksums(A, B)
     assert np.all(np.abs(C.sum(axis=1) - row) <= 4.0 * K * TWO_M24 * rowabs + 1e-9 * rowabs + N * 1e-12)
     assert np.all(np.abs(C.sum(axis=0) - col) <= 4.0 * K * TWO_M24 * colabs + 1e-9 * colabs + M * 1e-12)
+
+
+def test_splitk_graph_capture_replays():
+    """Both launches of a split-K call (slices, then the sum) captured into a
+    HIP graph replay correctly, many times, with the workspace and C dirtied
+    and eager work between replays."""
+    cases = [(96, 96, 2048, 8), (256, 256, 8192, 16)]
+    ins = []
+    for i, (M, N, K, s) in enumerate(cases):
+        A, B, _ = wl.random_matrices(M, N, K, "int4", 20 + i)
+        ws = torch.empty(tg.tgemm_sgemm_splitk_workspace_size(M, N, K, s), dtype=torch.uint8, device="cuda")
+        ins.append((dev(A), dev(B), torch.empty((M, N), device="cuda"), ws, s, oracle.gemm_i64(A, B)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up outside the capture
+        for dA, dB, dC, ws, s, _ in ins:
+            tg.sgemm_splitk(dA, dB, out=dC, splits=s, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for dA, dB, dC, ws, s, _ in ins:
+            tg.sgemm_splitk(dA, dB, out=dC, splits=s, workspace=ws)
+    for rep in range(5):
+        for _, _, dC, ws, _, _ in ins:
+            dC.fill_(float("nan"))
+            ws.fill_(0xFF)  # NaN patterns in every partial block
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, _, dC, _, s, Pi) in ins:
+            C = dC.cpu().numpy()
+            if not np.array_equal(C.astype(np.float64), Pi.astype(np.float64)):
+                pytest.fail(f"replay {rep}, splits {s}: result differs from the exact product")
+        x = torch.randn(1024, 1024, device="cuda")
+        _ = (x @ x).sum().item()
+
+
+def test_splitk_two_streams_two_workspaces():
+    """Two split-K products in flight at once on two streams, each with its
+    own workspace, give the same results as alone."""
+    M, N, K = 256, 256, 16384
+    (A1, B1, _), (A2, B2, _) = (wl.random_matrices(M, N, K, "int4", 30 + i) for i in range(2))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    d = [(dev(A1), dev(B1)), (dev(A2), dev(B2))]
+    outs = [torch.empty((M, N), device="cuda") for _ in range(2)]
+    need = tg.tgemm_sgemm_splitk_workspace_size(M, N, K, 16)
+    wss = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for (dA, dB), out, ws, st in zip(d, outs, wss, (s1, s2)):
+            tg.sgemm_splitk(dA, dB, out=out, splits=16, workspace=ws, stream=st.cuda_stream)
+        torch.cuda.synchronize()
+        assert_exact(outs[0].cpu().numpy(), oracle.gemm_i64(A1, B1), f"stream 1, rep {rep}")
+        assert_exact(outs[1].cpu().numpy(), oracle.gemm_i64(A2, B2), f"stream 2, rep {rep}")
