@@ -11,6 +11,7 @@ and reported alongside, since the headline metric covers both sizes.
                   [--also NAME,...] [--no-cpu-baseline] [--copy-bytes N]
   python bench.py --transpose blocked|naive|tiled|tiled_padded [--workload NAME]
   python bench.py --host [--workload NAME] [--panel-rows R]
+  python bench.py --shape MxNxK --kernel splitk[S] --also ''   (K split across work-groups)
 
 With --transpose the line measures B = Aᵀ (tgemm_transpose) instead, default
 workload 16384×16384: GB/s of algorithmic traffic (every element read once
@@ -112,7 +113,10 @@ def parse():
                    help="keep warming up (untimed) until this much time has passed, so the GPU "
                         "clock has settled before the timed steps")
     p.add_argument("--workload", default="square8192_uniform")
-    p.add_argument("--kernel", default="auto")
+    p.add_argument("--kernel", default="auto",
+                   help="auto | naive | simt | lds<T>[p1] | mfma:<variant> | splitk[<slices>]")
+    p.add_argument("--shape", default=None,
+                   help="MxNxK: time a U[-1,1) product of that shape (seed 0) instead of --workload")
     p.add_argument("--also", default="square4096_uniform",
                    help="comma-separated extra workloads timed the same way ('' for none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,6 +163,25 @@ def kernel_call(name: str):
         pad = 1 if name.endswith("p1") else 0
         return ((lambda A, B, C: tg.sgemm(A, B, out=C, kernel="lds", tile=tile, pad=pad)),
                 f"tgemm_sgemm_lds(tile={tile},pad={pad})")
+    if name.startswith("splitk"):
+        # tgemm_sgemm_splitk with `splits` slices ("splitk8") or the library's
+        # choice ("splitk"); the workspace is allocated on the first call,
+        # which is a warm-up call, outside any timed region
+        splits = int(name[6:]) if name[6:] else None
+        state = {}
+
+        def call(A, B, C):
+            import torch
+
+            if "ws" not in state:
+                M, K = A.shape
+                N = B.shape[1]
+                state["s"] = splits or tg.tgemm_sgemm_splitk_choose(M, N, K)
+                need = tg.tgemm_sgemm_splitk_workspace_size(M, N, K, state["s"])
+                state["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+            return tg.sgemm_splitk(A, B, out=C, splits=state["s"], workspace=state["ws"])
+
+        return call, f"tgemm_sgemm_splitk(splits={splits if splits else 'chosen'})"
     if name.startswith("mfma:"):
         v = name.split(":", 1)[1]
         names = tg.variant_names()
@@ -599,7 +622,11 @@ def main():
     if args.host:
         return host_main(args, props)
 
-    w = wl.WORKLOADS[args.workload]
+    if args.shape:
+        M, N, K = (int(x) for x in args.shape.lower().split("x"))
+        w = wl.Workload(f"shape{M}x{N}x{K}_uniform", M, N, K, "uniform", 0)
+    else:
+        w = wl.WORKLOADS[args.workload]
     m = time_workload(w, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,
                       args.op_a, args.op_b)
     plain = args.kernel == "auto" and args.op_a == "N" and args.op_b == "N" and not args.cold
@@ -651,7 +678,7 @@ def main():
             "frac_of_peak_at_this_clock": round(achieved / at_clock, 4),
         }
     # the vendor library computes the plain product; compare only what it computes
-    vendor = not args.no_vendor and args.kernel == "auto" and not args.cold
+    vendor = not args.no_vendor and (args.kernel == "auto" or args.kernel.startswith("splitk")) and not args.cold
     if vendor:
         line["vendor_blas"] = vendor_blas(m, args.steps, args.warmup_seconds)
     also = {}
