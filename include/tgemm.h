@@ -100,7 +100,8 @@ tgemm_status_t tgemm_sgemm_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64
                               float *C, int64_t ldc, hipStream_t stream);
 
 /*
- * C = A·B (row-major operands, as tgemm_sgemm) with the k range split
+ * C = A·B (row-major operands, as tgemm_sgemm; transposed ones through
+ * tgemm_sgemm_splitk_ex below) with the k range split
  * across work-groups: the sum over k of page 1's section [Matrix
  * Multiplication] taken in up to `splits` contiguous slices that run side by
  * side, each slice's partial product written to its own M×N block of
@@ -124,6 +125,18 @@ tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K,
                                   const float *B, int64_t ldb,
                                   float *C, int64_t ldc, int splits,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tgemm_sgemm_splitk with operands stored transposed, as tgemm_sgemm_ex
+ * (op_a / op_b = TGEMM_OP_T: A stored K×M, B stored N×K); the same
+ * workspace.  tgemm_sgemm_splitk(...) is tgemm_sgemm_splitk_ex(TGEMM_OP_N,
+ * TGEMM_OP_N, ...).
+ */
+tgemm_status_t tgemm_sgemm_splitk_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                                     const float *A, int64_t lda,
+                                     const float *B, int64_t ldb,
+                                     float *C, int64_t ldc, int splits,
+                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes tgemm_sgemm_splitk needs: splits·M·N·4; 0 when splits <= 1,
  * splits > 64 or a size is not positive or above 2^31-2^16. */

@@ -343,3 +343,19 @@ def test_splitk_argument_checks(lib):
     # empty products finish without a launch, whatever the workspace
     assert tg.tgemm_sgemm_splitk(0, N, K, A_, K, B_, N, C_, N, 4, None, 0, None) == tg.TGEMM_SUCCESS
     assert tg.tgemm_sgemm_splitk(M, 0, K, A_, K, B_, 1, C_, 1, 4, None, 0, None) == tg.TGEMM_SUCCESS
+
+
+def test_splitk_ex_argument_checks(lib):
+    M, N, K = 64, 64, 4096
+    W_ = 0x40000000
+    need = tg.tgemm_sgemm_splitk_workspace_size(M, N, K, 4)
+    for op in (2, -1):
+        assert tg.tgemm_sgemm_splitk_ex(op, N_, M, N, K, A_, K, B_, N, C_, N, 4, W_, need, None) == UNSUPPORTED
+        assert tg.tgemm_sgemm_splitk_ex(N_, op, M, N, K, A_, K, B_, N, C_, N, 4, W_, need, None) == UNSUPPORTED
+    # Aᵀ stored K×M: lda must reach M, not K
+    assert tg.tgemm_sgemm_splitk_ex(T_, N_, M, N, K, A_, M - 1, B_, N, C_, N, 4, W_, need, None) == INVALID
+    # Bᵀ stored N×K: ldb must reach K
+    assert tg.tgemm_sgemm_splitk_ex(N_, T_, M, N, K, A_, K, B_, K - 1, C_, N, 4, W_, need, None) == INVALID
+    # the workspace may not overlap a transposed A's K×M extent
+    assert tg.tgemm_sgemm_splitk_ex(T_, N_, M, N, K, A_, M, B_, N, C_, N, 4, A_ + 4 * M * (K - 1), need,
+                                    None) == INVALID

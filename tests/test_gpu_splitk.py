@@ -222,3 +222,15 @@ def test_splitk_two_streams_two_workspaces():
         torch.cuda.synchronize()
         assert_exact(outs[0].cpu().numpy(), oracle.gemm_i64(A1, B1), f"stream 1, rep {rep}")
         assert_exact(outs[1].cpu().numpy(), oracle.gemm_i64(A2, B2), f"stream 2, rep {rep}")
+
+
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("M,N,K,splits", [(96, 80, 2048, 8), (65, 33, 3000, 4), (256, 256, 16384, None)])
+def test_splitk_transposed_operands_integer_exact(ta, tb, M, N, K, splits):
+    log(f"splitk transposed ta={ta} tb={tb} {M}x{N}x{K} splits={splits}")
+    A, B, _ = wl.random_matrices(M, N, K, "int4", 40)
+    dA = dev(A.T).t() if ta else dev(A)
+    dB = dev(B.T).t() if tb else dev(B)
+    C = tg.sgemm_splitk(dA, dB, splits=splits)
+    torch.cuda.synchronize()
+    assert_exact(C.cpu().numpy(), oracle.gemm_i64(A, B), f"ta={ta} tb={tb} {M}x{N}x{K}")

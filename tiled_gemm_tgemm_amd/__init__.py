@@ -38,6 +38,7 @@ from ._lib import (  # noqa: F401
     tgemm_sgemm_host,
     tgemm_sgemm_host_workspace_size,
     tgemm_sgemm_splitk,
+    tgemm_sgemm_splitk_ex,
     tgemm_sgemm_splitk_choose,
     tgemm_sgemm_splitk_workspace_size,
     tgemm_sgemm_variant_for,
@@ -124,9 +125,10 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
 
 
 def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
-    """C = A·B for row-major float32 CUDA tensors with K split across
-    work-groups (tgemm_sgemm_splitk), for shapes with few output tiles and a
-    long K.  splits: None for the library's choice (tgemm_sgemm_splitk_choose),
+    """C = A·B for float32 CUDA tensors with K split across work-groups
+    (tgemm_sgemm_splitk_ex), for shapes with few output tiles and a long K.
+    A and B may be row-major or transposed views of row-major matrices, as
+    for sgemm.  splits: None for the library's choice (tgemm_sgemm_splitk_choose),
     else 1 ... 64.  workspace: a CUDA uint8 tensor of at least
     tgemm_sgemm_splitk_workspace_size bytes (allocated if omitted; two calls
     in flight at once need two).  Queued on `stream` (default: torch's current
@@ -141,8 +143,6 @@ def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
         raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     op_a, lda = _layout(A, "A")
     op_b, ldb = _layout(B, "B")
-    if (op_a, op_b) != (TGEMM_OP_N, TGEMM_OP_N):
-        raise ValueError("sgemm_splitk takes row-major operands only")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     else:
@@ -161,10 +161,10 @@ def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
         raise TypeError("workspace must be a CUDA uint8 tensor")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
-    st = tgemm_sgemm_splitk(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, splits,
-                            workspace.data_ptr(), workspace.numel(), stream)
+    st = tgemm_sgemm_splitk_ex(op_a, op_b, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
+                               splits, workspace.data_ptr(), workspace.numel(), stream)
     if st != TGEMM_SUCCESS:
-        raise TgemmError(st, "tgemm_sgemm_splitk")
+        raise TgemmError(st, "tgemm_sgemm_splitk_ex")
     return out
 
 

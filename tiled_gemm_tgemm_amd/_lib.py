@@ -47,6 +47,8 @@ SIGNATURES = {
     "tgemm_sgemm_host": (ctypes.c_int, _GEMM + [_ptr, _i64, _i64, _ptr, _ptr, _ptr]),
     "tgemm_sgemm_host_workspace_size": (_i64, [_i64, _i64, _i64, _i64]),
     "tgemm_sgemm_splitk": (ctypes.c_int, _GEMM + [ctypes.c_int, _ptr, ctypes.c_size_t, _ptr]),
+    "tgemm_sgemm_splitk_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + _GEMM
+                              + [ctypes.c_int, _ptr, ctypes.c_size_t, _ptr]),
     "tgemm_sgemm_splitk_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int]),
     "tgemm_sgemm_splitk_choose": (ctypes.c_int, [_i64, _i64, _i64]),
     "tgemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -130,6 +132,12 @@ def tgemm_sgemm_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, works
                        stream=None) -> int:
     return library().tgemm_sgemm_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
                                         workspace_bytes, stream)
+
+
+def tgemm_sgemm_splitk_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspace_bytes,
+                          stream=None) -> int:
+    return library().tgemm_sgemm_splitk_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
+                                           workspace_bytes, stream)
 
 
 def tgemm_sgemm_splitk_workspace_size(M, N, K, splits) -> int:

@@ -158,12 +158,13 @@ double sum_cycles(int64_t M, int64_t N, int slices)
 }
 
 // Best configuration for exactly up to `splits` slices (splits >= 2).
-Split choose_split(int64_t M, int64_t N, int64_t K, bool vec4, int64_t lda, int64_t ldb, int splits)
+Split choose_split(bool ta, bool tb, int64_t M, int64_t N, int64_t K, bool vec4, int64_t lda, int64_t ldb,
+                   int splits)
 {
     Split best;
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
-        if (!v->split_k || !runs(*v, vec4, false, false, lda, ldb)) continue;
+        if (!v->split_k || !runs(*v, vec4, ta, tb, lda, ldb)) continue;
         const int64_t kc = kchunk_for(*v, K, splits);
         const int64_t slices = (K + kc - 1) / kc;
         const int64_t tiles = ((M + v->bm - 1) / v->bm) * ((N + v->bn - 1) / v->bn);
@@ -271,7 +272,7 @@ int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K)
     // 384×640×4096, 23.7 µs with 4 slices against 30.4 with 16)
     int pick = 1;
     for (int splits = 2; splits <= kMaxSplits && (K + splits - 1) / splits >= kMinSliceK; splits *= 2) {
-        const Split sp = choose_split(M, N, K, true, max1(K), max1(N), splits);
+        const Split sp = choose_split(false, false, M, N, K, true, max1(K), max1(N), splits);
         if (sp.variant >= 0 && sp.slices > 1 && (best < 0 || sp.cycles < best)) {
             best = sp.cycles;
             pick = splits;
@@ -280,17 +281,20 @@ int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K)
     return pick;
 }
 
-tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
-                                  const float *B, int64_t ldb, float *C, int64_t ldc, int splits,
-                                  void *workspace, size_t workspace_bytes, hipStream_t stream)
+tgemm_status_t tgemm_sgemm_splitk_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                                     const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                                     int64_t ldc, int splits, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream)
 {
+    if (!op_ok(op_a) || !op_ok(op_b)) return TGEMM_ERROR_NOT_SUPPORTED;
+    const bool ta = op_a == TGEMM_OP_T, tb = op_b == TGEMM_OP_T;
     Quick quick;
-    const tgemm_status_t st = validate(false, false, M, N, K, A, lda, B, ldb, C, ldc, quick);
+    const tgemm_status_t st = validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick);
     if (st != TGEMM_SUCCESS) return st;
     if (splits < 1 || splits > kMaxSplits) return TGEMM_ERROR_INVALID_VALUE;
     if (quick == Quick::kDone) return TGEMM_SUCCESS;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
-    if (splits == 1) return tgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream);
+    if (splits == 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
     // the workspace: `splits` blocks of M×N floats, 16-byte aligned, apart from A, B and C
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 ||
         workspace_bytes < tgemm_sgemm_splitk_workspace_size(M, N, K, splits))
@@ -299,15 +303,15 @@ tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *
     if (workspace_bytes > UINTPTR_MAX - w0) return TGEMM_ERROR_INVALID_VALUE;
     const uintptr_t w1 = w0 + workspace_bytes;
     uintptr_t x0, x1;
-    if (span(A, M, K, lda, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
-    if (span(B, K, N, ldb, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    if (span(A, ta ? K : M, ta ? M : K, lda, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    if (span(B, tb ? N : K, tb ? K : N, ldb, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
     if (span(C, M, N, ldc, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
-    const bool vec4 = vec4_ok(false, false, M, N, K, A, lda, B, ldb);
-    const Split sp = choose_split(M, N, K, vec4, lda, ldb, splits);
+    const bool vec4 = vec4_ok(ta, tb, M, N, K, A, lda, B, ldb);
+    const Split sp = choose_split(ta, tb, M, N, K, vec4, lda, ldb, splits);
     if (sp.variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
-    if (sp.slices <= 1) return tgemm_sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream);
+    if (sp.slices <= 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
     float *W = static_cast<float *>(workspace);
-    GemmArgs g = pack(false, false, M, N, K, A, lda, B, ldb, W, N);
+    GemmArgs g = pack(ta, tb, M, N, K, A, lda, B, ldb, W, N);
     g.splits = sp.slices;
     g.kchunk = sp.kchunk;
     g.c_slice = M * N;
@@ -315,6 +319,14 @@ tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *
     const hipError_t e = v->launch(g, stream);
     if (e != hipSuccess) return TGEMM_ERROR_HIP;
     return from_hip(tgemm::launch_splitk_sum((int)M, (int)N, sp.slices, W, C, ldc, stream));
+}
+
+tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                                  const float *B, int64_t ldb, float *C, int64_t ldc, int splits,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return tgemm_sgemm_splitk_ex(TGEMM_OP_N, TGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
+                                 workspace_bytes, stream);
 }
 
 int tgemm_mfma_variant_count(void) { return tgemm::mfma_variant_count(); }
