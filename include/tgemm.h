@@ -139,7 +139,8 @@ tgemm_status_t tgemm_sgemm_splitk_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M
                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes tgemm_sgemm_splitk needs: splits·M·N·4; 0 when splits <= 1,
- * splits > 64 or a size is not positive or above 2^31-2^16. */
+ * splits > 64, a size is not positive or above 2^31-2^16, or the product does
+ * not fit in a size_t. */
 size_t tgemm_sgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int splits);
 
 /* The split count (1, 2, 4, ..., 64) the library's cost model expects to be

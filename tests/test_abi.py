@@ -359,3 +359,13 @@ def test_splitk_ex_argument_checks(lib):
     # the workspace may not overlap a transposed A's K×M extent
     assert tg.tgemm_sgemm_splitk_ex(T_, N_, M, N, K, A_, M, B_, N, C_, N, 4, A_ + 4 * M * (K - 1), need,
                                     None) == INVALID
+
+
+def test_splitk_workspace_size_never_wraps(lib):
+    # 64·(2^31 - 2^16)²·4 bytes does not fit in 64 bits: reported as 0, and a
+    # call with any workspace is refused before anything is queued
+    assert tg.tgemm_sgemm_splitk_workspace_size(MAX_DIM, MAX_DIM, 4096, 64) == 0
+    assert tg.tgemm_sgemm_splitk_workspace_size(MAX_DIM, MAX_DIM, 4096, 2) == 0     # 2^65 bytes
+    assert tg.tgemm_sgemm_splitk_workspace_size(MAX_DIM, 1 << 20, 4096, 64) == 64 * MAX_DIM * (1 << 20) * 4
+    assert tg.tgemm_sgemm_splitk(MAX_DIM, MAX_DIM, 4096, 1 << 40, 4096, 1 << 41, MAX_DIM, 1 << 46, MAX_DIM,
+                                 64, 1 << 60, 2 ** 64 - 2 ** 61, None) == INVALID

@@ -253,7 +253,8 @@ size_t tgemm_sgemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int sp
 {
     if (M <= 0 || N <= 0 || K <= 0 || splits <= 1 || splits > kMaxSplits) return 0;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
-    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+    const unsigned __int128 bytes = (unsigned __int128)splits * (uint64_t)M * (uint64_t)N * sizeof(float);
+    return bytes > (unsigned __int128)SIZE_MAX ? 0 : (size_t)bytes;  // 0: no such workspace can exist
 }
 
 int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K)
@@ -296,8 +297,8 @@ tgemm_status_t tgemm_sgemm_splitk_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
     if (splits == 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
     // the workspace: `splits` blocks of M×N floats, 16-byte aligned, apart from A, B and C
-    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 ||
-        workspace_bytes < tgemm_sgemm_splitk_workspace_size(M, N, K, splits))
+    const size_t need = tgemm_sgemm_splitk_workspace_size(M, N, K, splits);
+    if (need == 0 || workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 || workspace_bytes < need)
         return TGEMM_ERROR_INVALID_VALUE;
     const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
     if (workspace_bytes > UINTPTR_MAX - w0) return TGEMM_ERROR_INVALID_VALUE;
