@@ -174,10 +174,9 @@ int tgemm_mfma_variant_count(void);
  * Static description of a variant, e.g. "m256n128k16_w2x2_vec4" (macro tile
  * 256×128, depth 16 per phase, 2×2 wavefronts, 16-byte loads),
  * "m32n32k32_w1x1s8_vec4" (32×32 tile staged through LDS, K split over 8
- * single-wavefront slices), "m32n32k8_s4d4_vec4" (32×32 tile read straight
- * from device memory, K split over 4 wavefronts, 4 groups of 8 in flight),
- * "..._flat" (64-bit pointers, any leading dimension, operands as stored
- * only); NULL for an index out of range.
+ * single-wavefront slices), "..._nn" (operands as stored only: TGEMM_OP_T is
+ * refused), "..._flat" (64-bit pointers, any leading dimension, operands as
+ * stored only); NULL for an index out of range.
  */
 const char *tgemm_mfma_variant_name(int variant);
 

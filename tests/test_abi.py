@@ -60,7 +60,7 @@ def test_static_queries(lib):
     n = tg.tgemm_mfma_variant_count()
     assert n >= 6
     names = tg.variant_names()
-    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_(w\dx\d(s\d)?|s\dd\d)_vec[14](_flat)?", x) for x in names)
+    assert len(set(names)) == n and all(re.fullmatch(r"m\d+n\d+k\d+_w\dx\d(s\d)?_vec[14](_flat|_nn)?", x) for x in names)
     assert tg.tgemm_mfma_variant_name(n) is None and tg.tgemm_mfma_variant_name(-1) is None
     for st in range(4):
         assert tg.tgemm_status_string(st)
@@ -149,8 +149,13 @@ def test_transposed_variant_choice(lib):
         v = tg.tgemm_sgemm_variant_for_ex(op_a, op_b, M, N, K, 1 << 40, lda, 1 << 44, ldb, 1 << 46, N)
         return names[v] if v >= 0 else None
 
-    assert chosen(T_, N_, 4096, 4096, 4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
-    assert chosen(N_, T_, 8192, 8192, 8192, 8192, 8192) == "m256n128k16_w2x2_vec4"
+    # Aᵀ·B goes to the one-wavefront-per-SIMD 256×256 tile, which keeps two
+    # register sets of staged loads (MI355X, 8192³: 153.0 against 148.2
+    # TFLOP/s for 256×128; 4096³: 151.4 against 146.5)
+    assert chosen(T_, N_, 4096, 4096, 4096, 4096, 4096) == "m256n256k16_w2x2_vec4"
+    assert chosen(T_, N_, 8192, 8192, 8192, 8192, 8192) == "m256n256k16_w2x2_vec4"
+    assert chosen(N_, T_, 4096, 4096, 4096, 4096, 4096) == "m256n128k16_w2x2_vec4"   # 151.7 against 150.8
+    assert chosen(N_, T_, 8192, 8192, 8192, 8192, 8192) == "m256n256k16_w2x2_vec4"
     assert chosen(T_, T_, 512, 512, 512, 512, 512) == "m32n32k32_w1x1s8_vec4"
     # Aᵀ with M not a multiple of 4: its stored rows cannot take 16-byte loads
     assert chosen(T_, N_, 4098, 4096, 4096, 4098, 4096).endswith("vec1")
@@ -159,8 +164,9 @@ def test_transposed_variant_choice(lib):
     # no configuration takes a transposed operand with an enormous leading dimension
     assert chosen(T_, N_, 64, 64, 64, 1 << 28, 64) is None
     assert tg.tgemm_sgemm_ex(T_, N_, 64, 64, 64, 1 << 40, 1 << 28, 1 << 44, 64, 1 << 46, 64, None) == UNSUPPORTED
-    # the 64-bit-pointer fallback takes operands as stored only
-    flat = [i for i, n in enumerate(names) if n.endswith("_flat")]
+    # the 64-bit-pointer fallback and the "_nn" configurations take operands as stored only
+    flat = [i for i, n in enumerate(names) if n.endswith("_flat") or n.endswith("_nn")]
+    assert any(n.endswith("_nn") for n in names)
     for v in flat:
         assert tg.tgemm_sgemm_mfma_ex(T_, N_, 64, 64, 64, 1 << 40, 64, 1 << 44, 64, 1 << 46, 64, v,
                                       None) == UNSUPPORTED
@@ -194,26 +200,31 @@ def test_variant_choice(lib):
         v = tg.tgemm_sgemm_variant_for(M, N, K, a, lda or K, 1 << 44, ldb or N, 1 << 46, ldc or N)
         return names[v] if v >= 0 else None
 
-    assert chosen(8192, 8192, 8192) == "m256n128k16_w2x2_vec4"
+    # MI355X: 8192³ 7.16-7.20 ms (256×256) against 7.18-7.19 (256×128) with 24%
+    # fewer bytes moved; 4096³ 905-909 µs (256×128) against 908-912 (256×256)
+    assert chosen(8192, 8192, 8192) == "m256n256k16_w2x2_vec4"
     assert chosen(4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
-    assert chosen(3000, 5000, 1000) == "m256n128k16_w2x2_vec4"
-    # 32×32 tiles with K split over eight wavefronts: 7.5 µs against 10.3 for
-    # the small-product kernel and 11.7 for 64×64 tiles on MI355X
+    assert chosen(16384, 5000, 8192) == "m256n256k16_w2x2_vec4"   # 8.96 ms against 9.03
+    assert chosen(8192, 4096, 1024) == "m256n128k16_w2x2_vec4"    # 472 µs against 477
+    # ragged: three rounds of 160×128 tiles, 228 µs against 235 for one of 256×128
+    assert chosen(3000, 5000, 1000) == "m160n128k16_w1x4_vec4_nn"
+    assert chosen(640, 8192, 1000) == "m64n64k32_w2x2_vec4"       # 78.3 µs against 84.6 for 160×128
+    # 32×32 tiles with K split over eight wavefronts: 7.3-7.5 µs against 11.7
+    # for 64×64 tiles on MI355X
     assert chosen(512, 512, 512) == "m32n32k32_w1x1s8_vec4"
     assert chosen(1024, 1024, 1024) == "m64n64k32_w2x2_vec4"
     assert chosen(2048, 2048, 2048) == "m128n128k32_w2x2_vec4"  # 123.6 µs vs 127.6 for 64×64
     assert chosen(640, 640, 640) == "m32n32k32_w1x1s4_vec4"     # 11.1 µs vs 13.6 for 64×64 on MI355X
     assert chosen(2500, 2500, 2500) == "m64n64k32_w2x2_vec4"    # 272 µs vs 305 for 128×128
     assert chosen(6144, 6144, 6144) == "m128n128k32_w2x2_vec4"
-    assert chosen(256, 256, 8192) == "m32n32k32_w1x1s8_vec4"    # 50.0 µs vs 80.5 small-product kernel
+    assert chosen(256, 256, 8192) == "m32n32k32_w1x1s8_vec4"    # 50.0 µs on MI355X
     assert chosen(2048, 256, 8192) == "m32n32k32_w1x1s4_vec4"   # 92.0 µs vs 131.2 for 64×64
-    assert chosen(2048, 256, 8192, a=(1 << 40) + 4) == "m32n32k32_w1x1s4_vec1"  # 153 µs vs 263 small-product
+    assert chosen(2048, 256, 8192, a=(1 << 40) + 4) == "m32n32k32_w1x1s4_vec1"  # 153 µs on MI355X
     assert chosen(64, 64, 64) == "m64n64k32_w2x2_vec4"          # 4.0 µs vs 5.0 for 32×32 tiles
-    # long K on few tiles: the unsplit 64×64 tile (133 µs on MI355X) ahead of
-    # the four-way K split inside the work-group (148 µs)
+    # long K on few tiles: the unsplit 64×64 tile (133 µs on MI355X)
     assert chosen(1024, 1024, 8192) == "m64n64k32_w2x2_vec4"
     assert chosen(300, 300, 300, lda=1 << 24).endswith("_flat")   # lda beyond 32-bit offsets
-    assert chosen(3000, 5000, 1000).endswith("vec4")
+    assert "vec4" in chosen(3000, 5000, 1000)
     assert chosen(7, 5, 3).endswith("vec1")          # K, N not multiples of 4
     assert chosen(64, 64, 64, a=(1 << 40) + 4).endswith("vec1")  # A not 16-byte aligned
     assert chosen(0, 4, 4) is None and chosen(4, 4, 0) is None

@@ -103,7 +103,7 @@ def vec4_shape(M, N, K):
 def runnable(name, M, N, K, ta=False, tb=False):
     """Whether variant `name` takes contiguous aligned operands of these
     shapes and orders (ta: A stored K×M, tb: B stored N×K)."""
-    if (ta or tb) and name.endswith("_flat"):
+    if (ta or tb) and (name.endswith("_flat") or name.endswith("_nn")):
         return False
     if "vec4" not in name:
         return True

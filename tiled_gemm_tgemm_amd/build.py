@@ -26,7 +26,7 @@ LIBRARY = os.path.join(HERE, "libtgemm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "host_pipeline.cpp", "naive.hip", "lds_tiled.hip", "simt_tiled.hip", "transpose.hip", "splitk_sum.hip",
-           "mfma_sgemm.hip", "mfma_sgemm_small.hip", "mfma_sgemm_flat.hip"]
+           "mfma_sgemm.hip", "mfma_sgemm_flat.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wextra",

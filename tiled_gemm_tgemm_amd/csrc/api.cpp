@@ -109,7 +109,9 @@ bool runs(const tgemm::MfmaVariant &v, bool vec4, bool ta, bool tb, int64_t lda,
 // leave CUs less full, and is costed at its own residency.  Edge tiles cost
 // as much as full ones, which is what makes smaller tiles win on small or
 // ragged shapes.
-double cost_tiles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t K)
+// `order`: the configuration's relative rate for this operand order (its
+// tn_factor for Aᵀ·B, else 1).
+double cost_tiles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t K, double order = 1.0)
 {
     const int64_t cus = 256;
     const int64_t full_rounds = tiles / (cus * v.wg_per_cu);
@@ -117,8 +119,8 @@ double cost_tiles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t K)
     const double kpad = (double)((K + v.bk - 1) / v.bk) * v.bk;
     const double per_wg = 2.0 * v.bm * v.bn * kpad / 4.0 / 64.0;
     auto eff = [&](int64_t r) {
-        if (v.wg_per_cu <= 1) return v.eff_full;
-        return v.eff_alone + (v.eff_full - v.eff_alone) * (double)(r - 1) / (double)(v.wg_per_cu - 1);
+        if (v.wg_per_cu <= 1) return v.eff_full * order;
+        return (v.eff_alone + (v.eff_full - v.eff_alone) * (double)(r - 1) / (double)(v.wg_per_cu - 1)) * order;
     };
     double t = (double)full_rounds * ((double)v.wg_per_cu * per_wg / eff(v.wg_per_cu) + v.round_cycles);
     if (rest > 0) {
@@ -128,9 +130,27 @@ double cost_tiles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t K)
     return t;
 }
 
-double cost(const tgemm::MfmaVariant &v, int64_t M, int64_t N, int64_t K)
+// The tiles of the last round finish together and are written out with no
+// computation left to cover the stores: the bytes of C they hold, at about
+// 5 TB/s (measured on MI355X: 4096×4096×K takes 0.220 µs per unit of K plus
+// 14 µs, the 64 MB of C; 16 values of k take 17.9 µs in all).  Earlier
+// rounds' stores overlap the next round's work in part, which the fixed cost
+// per round stands for.  This is what lets a tile that spreads a ragged shape
+// over more, shorter rounds win (3000×1000×5000: 160×128 tiles, the last of
+// three rounds 248 tiles, 228 µs; 256×128, one round of 480 tiles, 235 µs).
+double final_store_cycles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t M, int64_t N)
 {
-    return cost_tiles(v, ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn), K);
+    const int64_t slots = (int64_t)256 * v.wg_per_cu;
+    const int64_t last = tiles % slots != 0 ? tiles % slots : (tiles < slots ? tiles : slots);
+    const double tile_bytes = (double)last * v.bm * v.bn * 4.0;
+    const double c_bytes = (double)M * N * 4.0;
+    return (tile_bytes < c_bytes ? tile_bytes : c_bytes) / 5.0e12 * 2.4e9;
+}
+
+double cost(const tgemm::MfmaVariant &v, bool ta, bool tb, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+    return cost_tiles(v, tiles, K, (ta && !tb) ? v.tn_factor : 1.0) + final_store_cycles(v, tiles, M, N);
 }
 
 // K split across work-groups.  Slices are a whole number of a configuration's
@@ -168,7 +188,8 @@ Split choose_split(bool ta, bool tb, int64_t M, int64_t N, int64_t K, bool vec4,
         const int64_t kc = kchunk_for(*v, K, splits);
         const int64_t slices = (K + kc - 1) / kc;
         const int64_t tiles = ((M + v->bm - 1) / v->bm) * ((N + v->bn - 1) / v->bn);
-        const double c = cost_tiles(*v, tiles * slices, kc) + (slices > 1 ? sum_cycles(M, N, (int)slices) : 0.0);
+        const double c = cost_tiles(*v, tiles * slices, kc, (ta && !tb) ? v->tn_factor : 1.0) +
+                         (slices > 1 ? sum_cycles(M, N, (int)slices) : 0.0);
         if (best.variant < 0 || c < best.cycles) {
             best.variant = i;
             best.slices = (int)slices;
@@ -191,7 +212,7 @@ int choose_variant(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const floa
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
         if (!runs(*v, vec4, ta, tb, lda, ldb)) continue;
-        const double c = cost(*v, M, N, K);
+        const double c = cost(*v, ta, tb, M, N, K);
         if (best < 0 || c < best_cost) {
             best = i;
             best_cost = c;
@@ -265,7 +286,7 @@ int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K)
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
         if (!runs(*v, true, false, false, max1(K), max1(N))) continue;
-        const double c = cost(*v, M, N, K);
+        const double c = cost(*v, false, false, M, N, K);
         if (best < 0 || c < best) best = c;
     }
     // slices shorter than ~1024 values of k lose more to each work-group's

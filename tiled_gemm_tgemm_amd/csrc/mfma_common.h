@@ -58,6 +58,15 @@ __device__ __forceinline__ f32x4 read_frag(const float *base, int off)
     }
 }
 
+// Word distance from a lane's fragment of k-group 0 to its fragment of k-group
+// g in the same slice: 8g values of k further along a KC row, or 8g rows
+// further down an MC slice (row stride S).
+template <bool KC, int S>
+__device__ __forceinline__ constexpr int group_step(int g)
+{
+    return KC ? 8 * g : 8 * g * S;
+}
+
 // One wavefront's fragments of one k-group: a[i] for its FM row blocks of A,
 // b[j] for its FN column blocks of B.
 template <int FM, int FN, bool A_KC, int AS, bool B_KC, int BS>
@@ -65,13 +74,17 @@ struct Fragments {
     f32x4 a[FM];
     f32x4 b[FN];
 
+    // a_off / b_off: the offsets of k-group 0 (frag_offset with g = 0); the
+    // step to group g is a compile-time constant once the caller's loop over
+    // groups is unrolled, so it folds into the LDS reads' immediate offsets
+    // and only group 0's offsets occupy registers.
     __device__ __forceinline__ void read(const float *as, const float *bs, const int (&a_off)[FM],
-                                         const int (&b_off)[FN])
+                                         const int (&b_off)[FN], int g)
     {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[i] = read_frag<A_KC, AS>(as, a_off[i]);
+        for (int i = 0; i < FM; ++i) a[i] = read_frag<A_KC, AS>(as, a_off[i] + group_step<A_KC, AS>(g));
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = read_frag<B_KC, BS>(bs, b_off[j]);
+        for (int j = 0; j < FN; ++j) b[j] = read_frag<B_KC, BS>(bs, b_off[j] + group_step<B_KC, BS>(g));
     }
 };
 
@@ -98,17 +111,17 @@ __device__ __forceinline__ int frag_offset(int mn, int g, int half)
 }
 
 // A whole phase of BK values of k from one LDS stage; the reads of group
-// g+1 are issued before the matrix-core steps of group g.  a_off[g][i] and
-// b_off[g][j] come from frag_offset.
+// g+1 are issued before the matrix-core steps of group g.  a_off[i] and
+// b_off[j] are the k-group 0 offsets from frag_offset.
 template <int FM, int FN, int BK, bool A_KC, int AS, bool B_KC, int BS>
 __device__ __forceinline__ void mfma_phase(f32x16 (&acc)[FM][FN], const float *as, const float *bs,
-                                           const int (&a_off)[BK / 8][FM], const int (&b_off)[BK / 8][FN])
+                                           const int (&a_off)[FM], const int (&b_off)[FN])
 {
     Fragments<FM, FN, A_KC, AS, B_KC, BS> f[2];
-    f[0].read(as, bs, a_off[0], b_off[0]);
+    f[0].read(as, bs, a_off, b_off, 0);
 #pragma unroll
     for (int g = 0; g < BK / 8; ++g) {
-        if (g + 1 < BK / 8) f[(g + 1) & 1].read(as, bs, a_off[g + 1], b_off[g + 1]);
+        if (g + 1 < BK / 8) f[(g + 1) & 1].read(as, bs, a_off, b_off, g + 1);
         mfma_group<FM, FN>(acc, f[g & 1]);
     }
 }

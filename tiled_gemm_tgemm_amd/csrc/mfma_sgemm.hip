@@ -168,7 +168,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const float *base, int6
 //   MC: mn-contiguous (B as stored, A transposed): element (mn, k) at
 //       ptr[k*ld + mn]; LDS keeps [k][mn], row stride MN+8.
 // Each thread owns L slots of VEC consecutive elements along the contiguous
-// dimension; consecutive threads own consecutive slots of a row.
+// dimension; consecutive threads own consecutive slots of a row, and one pass
+// of all threads covers R whole rows.  When R does not divide the slice's
+// rows (PART: a 160-row slice is 2.5 passes of 64), the last pass covers only
+// the threads whose row lies inside the slice; for the others that slot reads
+// nothing (offset past every extent) and is not written to LDS.
 template <bool KC_, int MN, int BK, int VEC, int NT>
 struct Loader {
     static constexpr bool KC = KC_;
@@ -176,14 +180,16 @@ struct Loader {
     static constexpr int COLS = KC ? BK : MN;           // contiguous extent of a row
     static constexpr int S = KC ? BK + 4 : MN + 8;      // LDS row stride (words)
     static constexpr int WORDS = ROWS * S;              // one LDS stage
-    static constexpr int L = ROWS * COLS / (VEC * NT);  // slots per thread
     static constexpr int R = NT * VEC / COLS;           // rows between a thread's slots
-    static_assert((NT * VEC) % COLS == 0 && L >= 1 && L * R == ROWS, "slice splits into whole rows");
+    static constexpr int L = (ROWS + R - 1) / R;        // slots per thread
+    static constexpr bool PART = L * R != ROWS;         // the last pass is partial
+    static_assert((NT * VEC) % COLS == 0 && R >= 1 && L >= 1, "a pass of all threads covers whole rows");
 
     typedef typename Vec<VEC>::type vec_t;
     uint32_t off[L];  // byte offset of each slot from the slice's first element
     int c;            // contiguous coordinate of the thread's slots
     int st;           // LDS word offset of slot 0 (slot i adds i*R*S)
+    bool last_in;     // (PART) the thread's last slot lies inside the slice
     vec_t reg[L];
 
     // mn_valid: rows (KC) or columns (MC) of this tile inside the matrix.
@@ -191,10 +197,11 @@ struct Loader {
     {
         const int r0 = t * VEC / COLS;
         c = t * VEC % COLS;
+        last_in = !PART || r0 + (L - 1) * R < ROWS;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int r = r0 + i * R;
-            const bool in = KC ? r < mn_valid : c < mn_valid;
+            const bool in = (KC ? r < mn_valid : c < mn_valid) && (i < L - 1 || last_in);
             off[i] = in ? (uint32_t)((r * ld + c) * 4) : kOutside;
         }
         st = r0 * S + c;
@@ -235,7 +242,8 @@ struct Loader {
     __device__ __forceinline__ void store(float *stage) const
     {
 #pragma unroll
-        for (int i = 0; i < L; ++i) *reinterpret_cast<vec_t *>(stage + st + i * R * S) = reg[i];
+        for (int i = 0; i < L; ++i)
+            if (!PART || i < L - 1 || last_in) *reinterpret_cast<vec_t *>(stage + st + i * R * S) = reg[i];
     }
 };
 
@@ -328,22 +336,23 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         const float *a_tile = A + (LA::KC ? (int64_t)m0 * lda : (int64_t)m0);
         const float *b_tile = B + (LB::KC ? (int64_t)n0 * ldb : (int64_t)n0);
 
+        // the accumulators start from the in-loop zero above, so that no
+        // zero vector is kept (or spilled) across the tile loop
         f32x16 acc[G::FM][G::FN];
+        const float fzero = __builtin_bit_cast(float, zero);
 #pragma unroll
         for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
+            for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(fzero);
 
-        int a_frag[G::BK / 8][G::FM], b_frag[G::BK / 8][G::FN];
+        // fragment offsets of k-group 0 (later groups add a constant step)
+        int a_frag[G::FM], b_frag[G::FN];
 #pragma unroll
-        for (int g = 0; g < G::BK / 8; ++g) {
+        for (int i = 0; i < G::FM; ++i)
+            a_frag[i] = mfma::frag_offset<LA::KC, LA::S>(wm * G::TM + i * 32 + l32, 0, half);
 #pragma unroll
-            for (int i = 0; i < G::FM; ++i)
-                a_frag[g][i] = mfma::frag_offset<LA::KC, LA::S>(wm * G::TM + i * 32 + l32, g, half);
-#pragma unroll
-            for (int j = 0; j < G::FN; ++j)
-                b_frag[g][j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, g, half);
-        }
+        for (int j = 0; j < G::FN; ++j)
+            b_frag[j] = mfma::frag_offset<LB::KC, LB::S>(wn * G::TN + j * 32 + l32, 0, half);
         // K range [kb, ke) of this thread's slice; `full` phases hold BK values
         // of k, `nphase` phases in all, and phase r is `cut` (its k range reaches
         // past ke: A's columns there are masked) from r = full on.  With K split,
@@ -394,13 +403,16 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
         Frag f[2];
         auto rd = [&] __device__(Frag &fr, int stage, int g) {
             const float *st = slds + stage * G::STAGE;
-            fr.read(st, st + G::A_STAGE, a_frag[g], b_frag[g]);
+            fr.read(st, st + G::A_STAGE, a_frag, b_frag, g);
         };
         // One phase r, computed from LDS stage r % 2 with register set s holding
         // phase r+1.  next: phase r+1 exists (write it, then the barrier); load:
         // phase r+1+NS exists (issue its loads into set s), load_last: it is the
-        // shorter one; whole: it is a whole phase (issue_whole).
-        auto phase = [&] __device__(int s, int r, bool next, bool load, bool load_last, bool whole) {
+        // shorter one; whole: it is a whole phase (issue_whole); ng: k-groups
+        // whose matrix-core steps run (the partial phase skips the groups that
+        // lie wholly past K: they would add products of zero padding to
+        // accumulators that start at +0, which changes no bit).
+        auto phase = [&] __device__(int s, int r, bool next, bool load, bool load_last, bool whole, int ng) {
             auto issue_next = [&] __device__() {
                 if (whole)
                     issue_whole(s, r + 1 + G::NS);
@@ -423,7 +435,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
                 if (g + 1 < NG) {
                     rd(f[(g + 1) & 1], r & 1, g + 1);
                     if (g == 0 && next) store(s, r + 1);
-                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                    if (g < ng) mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
                     if (g == 0)
                         mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
                     else
@@ -434,7 +446,7 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
                         rd(f[0], (r + 1) & 1, 0);
                     }
                     issue_next();
-                    mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
+                    if (g < ng) mfma::mfma_group<G::FM, G::FN>(acc, f[g & 1]);
                     mfma::interleave<NM, RD, 0x100, WR, 0x020, 2>();
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -456,14 +468,19 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
 #pragma unroll 1
         for (; p + 2 * G::NS < full; p += G::NS) {  // every phase loaded in here is a full one
 #pragma unroll
-            for (int s = 0; s < G::NS; ++s) phase(s, p + s, true, true, false, true);
+            for (int s = 0; s < G::NS; ++s) phase(s, p + s, true, true, false, true, NG);
         }
+        // k-groups of the partial phase that hold a k below K (without a K
+        // split; with one, every slice runs all groups)
+        const int ng_last = SPLIT ? NG : (K - full * G::BK + 7) / 8;
 #pragma unroll 1
         for (; p < nphase; p += G::NS) {
 #pragma unroll
             for (int s = 0; s < G::NS; ++s) {
                 const int r = p + s;
-                if (r < nphase) phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, cut(r + 1 + G::NS), false);
+                if (r < nphase)
+                    phase(s, r, r + 1 < nphase, r + 1 + G::NS < nphase, cut(r + 1 + G::NS), false,
+                          r == full ? ng_last : NG);
             }
         }
 
@@ -580,38 +597,68 @@ constexpr int64_t max_ld()
 
 // One tile shape (with KS slices of K per work-group) in its four operand
 // orders (NN, TN, NT, TT).
-template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1, int NS = 2, int W = 2>
+// W × WN wavefronts per K slice (W along M).  NS_TN: register sets for the
+// Aᵀ·B order (A stored transposed, B as stored), whose fragment reads keep
+// the most LDS addresses live.  TRANS: the shape also runs transposed
+// operands (a transposed slice must split into whole rows per pass too).
+template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1, int NS = 2, int W = 2, int NS_TN = NS,
+          int WN = W, bool TRANS = true>
 struct Shape {
     template <bool TA, bool TB>
-    using C = Cfg<BM, BN, BK, W, W, VEC, GM, OCC, TA, TB, KS, NS>;
+    using C = Cfg<BM, BN, BK, W, WN, VEC, GM, OCC, TA, TB, KS, (TA && !TB) ? NS_TN : NS>;
+    static constexpr bool trans = TRANS;
     static hipError_t launch(const GemmArgs &g, hipStream_t stream)
     {
-        switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
-            case 0: return launch_cfg<C<false, false>>(g, stream);
-            case 1: return launch_cfg<C<true, false>>(g, stream);
-            case 2: return launch_cfg<C<false, true>>(g, stream);
-            default: return launch_cfg<C<true, true>>(g, stream);
+        if constexpr (!TRANS) {
+            if (g.trans_a || g.trans_b) return hipErrorInvalidValue;
+            return launch_cfg<C<false, false>>(g, stream);
+        } else {
+            switch ((g.trans_a ? 1 : 0) + (g.trans_b ? 2 : 0)) {
+                case 0: return launch_cfg<C<false, false>>(g, stream);
+                case 1: return launch_cfg<C<true, false>>(g, stream);
+                case 2: return launch_cfg<C<false, true>>(g, stream);
+                default: return launch_cfg<C<true, true>>(g, stream);
+            }
         }
     }
 };
 
+// Largest leading dimensions of a shape's transposed operands (0 when it
+// takes none).
+template <class S>
+constexpr int64_t max_lda_t()
+{
+    if constexpr (S::trans)
+        return max_ld<typename S::template C<true, false>::LA>();
+    else
+        return 0;
+}
+template <class S>
+constexpr int64_t max_ldb_t()
+{
+    if constexpr (S::trans)
+        return max_ld<typename S::template C<false, true>::LB>();
+    else
+        return 0;
+}
+
 //             BM   BN  BK VEC GROUP_M OCC
-typedef Shape<256, 128, 16, 4, 4, 2> Large4;
+typedef Shape<256, 128, 16, 4, 4, 2, 1, 2, 2, 1> Large4;  // Aᵀ·B: one register set (two spill)
+// one wavefront per SIMD holding a 128×128 sub-tile (512 registers)
+typedef Shape<256, 256, 16, 4, 4, 1> Huge4;
 typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
+// 160 rows of A as stored (2.5 passes of 64); four wavefronts side by side, each 160×32
+typedef Shape<160, 128, 16, 4, 4, 2, 1, 2, 1, 2, 4, false> Wide4;
 typedef Shape<64, 64, 32, 4, 8, 4> Small4;
 typedef Shape<256, 128, 16, 1, 4, 2, 1, 1> Large1;  // one register set (two spill)
 typedef Shape<128, 128, 32, 1, 8, 2> Mid1;
 typedef Shape<64, 64, 32, 1, 8, 4> Small1;
-typedef Shape<64, 64, 32, 4, 8, 4, 2> Small4x2;  // K split over two groups of wavefronts
-typedef Shape<64, 64, 32, 4, 8, 4, 4> Small4x4;  // ... over four
-typedef Shape<64, 64, 32, 1, 8, 4, 2> Small1x2;
-typedef Shape<64, 64, 32, 1, 8, 4, 4> Small1x4;
 typedef Shape<32, 32, 32, 4, 8, 2, 4, 2, 1> Tiny4x4;  // one wavefront per K slice
 typedef Shape<32, 32, 32, 4, 8, 2, 8, 2, 1> Tiny4x8;
 typedef Shape<32, 32, 32, 1, 8, 2, 4, 2, 1> Tiny1x4;
 typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 
-#define TGEMM_VARIANT(name, S, alone, full, round)                                                  \
+#define TGEMM_VARIANT_TN(name, S, alone, full, round, tn)                                            \
     {                                                                                                \
         name, S::template C<false, false>::BM, S::template C<false, false>::BN,                     \
             S::template C<false, false>::BK * S::template C<false, false>::KS,                      \
@@ -619,43 +666,42 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
             wg_per_cu<typename S::template C<false, false>>(),                                      \
             max_ld<typename S::template C<false, false>::LA>(),                                     \
             max_ld<typename S::template C<false, false>::LB>(),                                     \
-            max_ld<typename S::template C<true, false>::LA>(),                                      \
-            max_ld<typename S::template C<false, true>::LB>(), true, alone, full, round, &S::launch, \
-            true                                                                                     \
+            max_lda_t<S>(), max_ldb_t<S>(), S::trans, alone, full, round, &S::launch, true, tn      \
     }
+#define TGEMM_VARIANT(name, S, alone, full, round) TGEMM_VARIANT_TN(name, S, alone, full, round, 1.0)
 
-// Efficiencies measured on MI355X: 256 tiles with K = 8192 (one work-group per
-// CU) and four full rounds with K = 4096, as fractions of the matrix-core peak
-// (last measured with whole-phase loads, the persistent grid and the
-// interleaved schedule for 4-byte loads; the model's picks are unchanged from
-// the previous figures except on one misaligned shape, and on 8 shapes with
-// K, N not multiples of 4 its pick is the fastest 4-byte configuration).
-// For the K-split configurations, efficiencies and the fixed cost per round
-// (which carries the slices' final sum) were chosen against a sweep of 23
-// shapes from 128³ to 8192³ so that the model's pick is the measured fastest
-// or within 1.5% of it.  With whole-phase loads and the persistent grid the
-// unsplit 64×64 configuration alone on a CU sped up most (1024×1024×8192:
-// 165 → 133 µs, now ahead of the four-way split at 148 µs), and its
-// efficiency alone was raised to match; a sweep of 20 shapes from 128³ to
-// 6144³ (square, ragged, long and short K) then finds the model's pick the
-// fastest or within 2% of it, apart from 128³ (5.5 µs against 5.1 µs).  The 4-byte-load flavours keep the
-// measured ratio to the 16-byte ones.  The 32×32 K-split configurations were
-// fitted to a sweep of 27 small, ragged, skinny and long-K shapes with both
-// load widths (one work-group per CU: 256 tiles with K = 16384; CU full: 512
-// tiles with K = 4096 and 8192; the fixed cost from 256³ and 512³), after
-// which every pick on that sweep is the fastest or within 3% of it, apart
-// from 300³ with 4-byte loads (4%).
+// Efficiencies measured on MI355X, as fractions of the matrix-core peak, with
+// one resident work-group per CU (alone) and with the CU full, plus a fixed
+// cost per round of work-groups (SIMD cycles); api.cpp adds the exposed store
+// of the last round.  Fitted to two sweeps of 76 shapes in all (64³ to
+// 16384×6144×8192: square, ragged, skinny, long and short K) timing every
+// configuration: the model's pick is the measured fastest or within 1.0% of
+// it on every one.  The one-wavefront-per-SIMD 256×256 tile runs level with
+// 256×128 (8192³: 7.16-7.20 ms against 7.18-7.19) while moving 24% fewer
+// bytes (3.49 against 4.57 GB a launch), pulls ahead as K grows (16384×5000×8192:
+// 8.96 against 9.03 ms) and falls behind at short K (8192×4096×1024: 477
+// against 472 µs), which its higher fixed cost per round expresses: one
+// work-group per CU leaves its pipeline fill uncovered.  256×128 with A
+// transposed keeps one register set of staged loads (two spill) and runs
+// 3% slower than as stored (tn 0.969: 148.2 against 153.0 TFLOP/s at 8192³),
+// so Aᵀ·B goes to the 256×256 tile (153.0).  The 160×128 tile sustains less
+// (0.89 alone, 0.93 full) but spreads 3000×1000×5000 over three rounds of
+// tiles instead of one of 256×128 tiles (at most three of 160×128 per CU:
+// 60 blocks of 32×32 against 64), 228 against 235 µs.  The 4-byte-load
+// flavours keep their measured ratio to the 16-byte ones; the 32×32
+// K-split configurations were fitted to a sweep of 27 small, ragged, skinny
+// and long-K shapes with both load widths (one work-group per CU: 256 tiles
+// with K = 16384; CU full: 512 tiles with K = 4096 and 8192; the fixed cost
+// from 256³ and 512³).
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT("m256n128k16_w2x2_vec4", Large4, 0.97, 0.97, 7000.0),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.96, 0.96, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.91, 7000.0),
-    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.93, 0.95, 7000.0),
-    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.84, 0.89, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.69, 0.86, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2s2_vec4", Small4x2, 0.60, 0.72, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2s4_vec4", Small4x4, 0.72, 0.72, 10000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2s2_vec1", Small1x2, 0.44, 0.55, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2s4_vec1", Small1x4, 0.55, 0.55, 10000.0),
+    TGEMM_VARIANT_TN("m256n128k16_w2x2_vec4", Large4, 0.977, 0.977, 7000.0, 0.969),
+    TGEMM_VARIANT("m256n256k16_w2x2_vec4", Huge4, 0.979, 0.979, 13000.0),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.965, 0.965, 7000.0),
+    TGEMM_VARIANT("m160n128k16_w1x4_vec4_nn", Wide4, 0.8855, 0.9294, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.93, 7000.0),
+    TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.937, 0.957, 7000.0),
+    TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.844, 0.895, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.69, 0.879, 7000.0),
     TGEMM_VARIANT("m32n32k32_w1x1s4_vec4", Tiny4x4, 0.45, 0.61, 9500.0),
     TGEMM_VARIANT("m32n32k32_w1x1s8_vec4", Tiny4x8, 0.60, 0.60, 11500.0),
     TGEMM_VARIANT("m32n32k32_w1x1s4_vec1", Tiny1x4, 0.24, 0.37, 12000.0),

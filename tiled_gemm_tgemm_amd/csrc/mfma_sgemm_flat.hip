@@ -127,16 +127,11 @@ void mfma_sgemm_flat_kernel(int M, int N, int K, const float *__restrict__ A, in
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-    int a_frag[G::BK / 8][G::FM], b_frag[G::BK / 8][G::FN];
+    int a_frag[G::FM], b_frag[G::FN];  // k-group 0; later groups add a constant step
 #pragma unroll
-    for (int g = 0; g < G::BK / 8; ++g) {
+    for (int i = 0; i < G::FM; ++i) a_frag[i] = mfma::frag_offset<true, G::AS>(wm * G::TM + i * 32 + l32, 0, half);
 #pragma unroll
-        for (int i = 0; i < G::FM; ++i)
-            a_frag[g][i] = mfma::frag_offset<true, G::AS>(wm * G::TM + i * 32 + l32, g, half);
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j)
-            b_frag[g][j] = mfma::frag_offset<false, G::BS>(wn * G::TN + j * 32 + l32, g, half);
-    }
+    for (int j = 0; j < G::FN; ++j) b_frag[j] = mfma::frag_offset<false, G::BS>(wn * G::TN + j * 32 + l32, 0, half);
     const int phases = (K + G::BK - 1) / G::BK;
     load_phase(0);
     store_phase(0, 0);

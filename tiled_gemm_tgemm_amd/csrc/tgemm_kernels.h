@@ -78,29 +78,25 @@ struct MfmaVariant {
     double eff_alone, eff_full, round_cycles;
     hipError_t (*launch)(const GemmArgs &g, hipStream_t stream);
     bool split_k = false;  // takes GemmArgs::splits > 1
+    // measured rate with A stored transposed and B as stored, relative to
+    // operands as stored (used only to rank configurations)
+    double tn_factor = 1.0;
 };
 
-// Tiled buffer-load kernels (mfma_sgemm.hip), the small-product kernel
-// (mfma_sgemm_small.hip) and the 64-bit-pointer fallback (mfma_sgemm_flat.hip).
+// Tiled buffer-load kernels (mfma_sgemm.hip) and the 64-bit-pointer fallback
+// (mfma_sgemm_flat.hip).
 int mfma_buffer_variant_count();
 const MfmaVariant *mfma_buffer_variant(int index);
-int mfma_small_variant_count();
-const MfmaVariant *mfma_small_variant(int index);
 int mfma_flat_variant_count();
 const MfmaVariant *mfma_flat_variant(int index);
 
 // All configurations, in that order.
-inline int mfma_variant_count()
-{
-    return mfma_buffer_variant_count() + mfma_small_variant_count() + mfma_flat_variant_count();
-}
+inline int mfma_variant_count() { return mfma_buffer_variant_count() + mfma_flat_variant_count(); }
 inline const MfmaVariant *mfma_variant(int index)
 {
     if (index < 0) return nullptr;
     if (index < mfma_buffer_variant_count()) return mfma_buffer_variant(index);
-    index -= mfma_buffer_variant_count();
-    if (index < mfma_small_variant_count()) return mfma_small_variant(index);
-    return mfma_flat_variant(index - mfma_small_variant_count());
+    return mfma_flat_variant(index - mfma_buffer_variant_count());
 }
 
 }  // namespace tgemm
