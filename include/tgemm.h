@@ -138,6 +138,32 @@ tgemm_status_t tgemm_sgemm_splitk_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M
                                      float *C, int64_t ldc, int splits,
                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the fixed device scratch behind tgemm_sgemm_splitk_noalloc. */
+#define TGEMM_SPLITK_NOALLOC_BYTES ((size_t)32 << 20)
+
+/*
+ * tgemm_sgemm_splitk_ex for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same product with the same kernels and slices, so the same
+ * results bit for bit, but the slices' partial products live in a fixed
+ * scratch array of TGEMM_SPLITK_NOALLOC_BYTES (32 MiB) that the library holds
+ * on each GPU it runs on until the process ends, not in a caller's
+ * workspace.  The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls whose work overlaps in time on one GPU (two streams, two
+ * threads) race and give wrong results, so serialise them.  Argument
+ * meaning, layout, ownership and errors as tgemm_sgemm_splitk_ex, with
+ * TGEMM_ERROR_NOT_SUPPORTED when tgemm_sgemm_splitk_workspace_size(M, N, K,
+ * splits) exceeds TGEMM_SPLITK_NOALLOC_BYTES (e.g. 1024×1024 with more than 8
+ * splits), and TGEMM_ERROR_HIP if the array's device address cannot be
+ * obtained on the current device.
+ */
+tgemm_status_t tgemm_sgemm_splitk_noalloc(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                                          const float *A, int64_t lda,
+                                          const float *B, int64_t ldb,
+                                          float *C, int64_t ldc, int splits, hipStream_t stream);
+
 /* Workspace bytes tgemm_sgemm_splitk needs: splits·M·N·4; 0 when splits <= 1,
  * splits > 64, a size is not positive or above 2^31-2^16, or the product does
  * not fit in a size_t. */

@@ -391,3 +391,27 @@ def test_splitk_choice_matches_the_measured_best():
     assert tg.tgemm_sgemm_splitk_choose(256, 256, 16384) == 16    # 26.6 µs; 4 slices 33.2
     assert tg.tgemm_sgemm_splitk_choose(2048, 2048, 8192) == 1    # unsplit 455 µs; 2 slices 466
     assert tg.tgemm_sgemm_splitk_choose(1024, 1024, 1024) == 1    # slices would be under 1024 long
+
+
+def test_splitk_noalloc_argument_checks(lib):
+    """The allocation-free split-K entry point checks as tgemm_sgemm_splitk_ex
+    does and refuses, before any device work, a product whose partial sums
+    would not fit its fixed scratch."""
+    M, N, K = 64, 64, 4096
+    cap = tg.TGEMM_SPLITK_NOALLOC_BYTES
+    assert cap == 32 << 20
+    for op in (2, -1):
+        assert tg.tgemm_sgemm_splitk_noalloc(op, N_, M, N, K, A_, K, B_, N, C_, N, 4, None) == UNSUPPORTED
+        assert tg.tgemm_sgemm_splitk_noalloc(N_, op, M, N, K, A_, K, B_, N, C_, N, 4, None) == UNSUPPORTED
+    for splits in (0, -1, 65):
+        assert tg.tgemm_sgemm_splitk_noalloc(N_, N_, M, N, K, A_, K, B_, N, C_, N, splits, None) == INVALID
+    assert tg.tgemm_sgemm_splitk_noalloc(N_, N_, M, N, K, A_, K - 1, B_, N, C_, N, 4, None) == INVALID
+    assert tg.tgemm_sgemm_splitk_noalloc(N_, N_, M, N, K, A_, K, B_, N, A_ + 8, N, 4, None) == INVALID
+    # beyond the scratch: 2048×2048 in 4 slices needs 64 MiB; 1024×1024 in 16 needs 64 MiB
+    assert tg.tgemm_sgemm_splitk_workspace_size(2048, 2048, 8192, 4) > cap
+    big = (1 << 40, 8192, 1 << 42, 2048, 1 << 44, 2048)
+    assert tg.tgemm_sgemm_splitk_noalloc(N_, N_, 2048, 2048, 8192, *big, 4, None) == UNSUPPORTED
+    assert tg.tgemm_sgemm_splitk_noalloc(N_, N_, 1024, 1024, 8192, 1 << 40, 8192, 1 << 42, 1024, 1 << 44,
+                                         1024, 16, None) == UNSUPPORTED
+    # empty products finish without a launch
+    assert tg.tgemm_sgemm_splitk_noalloc(N_, N_, 0, N, K, A_, K, B_, N, C_, N, 4, None) == tg.TGEMM_SUCCESS

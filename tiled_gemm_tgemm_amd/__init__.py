@@ -40,7 +40,9 @@ from ._lib import (  # noqa: F401
     tgemm_sgemm_splitk,
     tgemm_sgemm_splitk_ex,
     tgemm_sgemm_splitk_choose,
+    tgemm_sgemm_splitk_noalloc,
     tgemm_sgemm_splitk_workspace_size,
+    TGEMM_SPLITK_NOALLOC_BYTES,
     tgemm_sgemm_variant_for,
     tgemm_status_string,
     tgemm_transpose,
@@ -165,6 +167,38 @@ def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
                                splits, workspace.data_ptr(), workspace.numel(), stream)
     if st != TGEMM_SUCCESS:
         raise TgemmError(st, "tgemm_sgemm_splitk_ex")
+    return out
+
+
+def sgemm_splitk_noalloc(A, B, out, *, splits=None, stream=None):
+    """sgemm_splitk for callers that cannot allocate (tgemm_sgemm_splitk_noalloc):
+    the partial products live in the library's fixed per-GPU scratch of
+    TGEMM_SPLITK_NOALLOC_BYTES, so `out` must be given and nothing is
+    allocated; calls overlapping in time on one GPU race.  Queued on `stream`
+    (default: torch's current stream); returns `out` without waiting."""
+    import torch
+
+    A = _check(A, "A")
+    B = _check(B, "B")
+    out = _check(out, "out")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be {M}x{N}")
+    if out.stride(1) != 1 and N > 1:
+        raise ValueError("out must be row-major")
+    op_a, lda = _layout(A, "A")
+    op_b, ldb = _layout(B, "B")
+    if splits is None:
+        splits = tgemm_sgemm_splitk_choose(M, N, K)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    st = tgemm_sgemm_splitk_noalloc(op_a, op_b, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(),
+                                    max(out.stride(0), N, 1), splits, stream)
+    if st != TGEMM_SUCCESS:
+        raise TgemmError(st, "tgemm_sgemm_splitk_noalloc")
     return out
 
 

@@ -18,6 +18,8 @@ TGEMM_SUCCESS = 0
 TGEMM_ERROR_INVALID_VALUE = 1
 TGEMM_ERROR_NOT_SUPPORTED = 2
 TGEMM_ERROR_HIP = 3
+# size of the fixed device scratch behind tgemm_sgemm_splitk_noalloc (include/tgemm.h)
+TGEMM_SPLITK_NOALLOC_BYTES = 32 << 20
 
 # every function the header declares, with (restype, argtypes)
 _i64 = ctypes.c_int64
@@ -49,6 +51,7 @@ SIGNATURES = {
     "tgemm_sgemm_splitk": (ctypes.c_int, _GEMM + [ctypes.c_int, _ptr, ctypes.c_size_t, _ptr]),
     "tgemm_sgemm_splitk_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + _GEMM
                               + [ctypes.c_int, _ptr, ctypes.c_size_t, _ptr]),
+    "tgemm_sgemm_splitk_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + _GEMM + [ctypes.c_int, _ptr]),
     "tgemm_sgemm_splitk_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, ctypes.c_int]),
     "tgemm_sgemm_splitk_choose": (ctypes.c_int, [_i64, _i64, _i64]),
     "tgemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -138,6 +141,10 @@ def tgemm_sgemm_splitk_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, splits, w
                           stream=None) -> int:
     return library().tgemm_sgemm_splitk_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
                                            workspace_bytes, stream)
+
+
+def tgemm_sgemm_splitk_noalloc(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, splits, stream=None) -> int:
+    return library().tgemm_sgemm_splitk_noalloc(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, splits, stream)
 
 
 def tgemm_sgemm_splitk_workspace_size(M, N, K, splits) -> int:

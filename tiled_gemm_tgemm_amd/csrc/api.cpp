@@ -7,6 +7,9 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tgemm_kernels.h"
 
 namespace {
@@ -221,6 +224,67 @@ int choose_variant(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const floa
     return best;
 }
 
+// The split-K product once arguments are valid and splits > 1: checks the
+// workspace (`splits` blocks of M×N floats, 16-byte aligned, apart from A, B
+// and C), then the sliced product into it and the in-order sum into C.
+tgemm_status_t splitk_launch(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                             const float *B, int64_t ldb, float *C, int64_t ldc, int splits, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream)
+{
+    const tgemm_op_t op_a = ta ? TGEMM_OP_T : TGEMM_OP_N, op_b = tb ? TGEMM_OP_T : TGEMM_OP_N;
+    const size_t need = tgemm_sgemm_splitk_workspace_size(M, N, K, splits);
+    if (need == 0 || workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 || workspace_bytes < need)
+        return TGEMM_ERROR_INVALID_VALUE;
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
+    if (workspace_bytes > UINTPTR_MAX - w0) return TGEMM_ERROR_INVALID_VALUE;
+    const uintptr_t w1 = w0 + workspace_bytes;
+    uintptr_t x0, x1;
+    if (span(A, ta ? K : M, ta ? M : K, lda, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    if (span(B, tb ? N : K, tb ? K : N, ldb, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    if (span(C, M, N, ldc, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
+    const bool vec4 = vec4_ok(ta, tb, M, N, K, A, lda, B, ldb);
+    const Split sp = choose_split(ta, tb, M, N, K, vec4, lda, ldb, splits);
+    if (sp.variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
+    if (sp.slices <= 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    float *W = static_cast<float *>(workspace);
+    GemmArgs g = pack(ta, tb, M, N, K, A, lda, B, ldb, W, N);
+    g.splits = sp.slices;
+    g.kchunk = sp.kchunk;
+    g.c_slice = M * N;
+    const tgemm::MfmaVariant *v = tgemm::mfma_variant(sp.variant);
+    const hipError_t e = v->launch(g, stream);
+    if (e != hipSuccess) return TGEMM_ERROR_HIP;
+    return from_hip(tgemm::launch_splitk_sum((int)M, (int)N, sp.slices, W, C, ldc, stream));
+}
+
+// The fixed device scratch of tgemm_sgemm_splitk_noalloc: room for the
+// slices' partial products of callers that cannot allocate.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not a device address: kernels and
+// copies are given the address scratch_on_device() looked up instead.
+static __device__ __align__(256) float scratch[TGEMM_SPLITK_NOALLOC_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void *scratch_on_device()
+{
+    static std::atomic<void *> address[kMaxDevices];
+    static std::mutex lookup;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = address[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    std::lock_guard<std::mutex> hold(lookup);
+    p = address[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        address[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 bool op_ok(tgemm_op_t op) { return op == TGEMM_OP_N || op == TGEMM_OP_T; }
 
 }  // namespace
@@ -317,30 +381,7 @@ tgemm_status_t tgemm_sgemm_splitk_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M
     if (quick == Quick::kDone) return TGEMM_SUCCESS;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
     if (splits == 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
-    // the workspace: `splits` blocks of M×N floats, 16-byte aligned, apart from A, B and C
-    const size_t need = tgemm_sgemm_splitk_workspace_size(M, N, K, splits);
-    if (need == 0 || workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 || workspace_bytes < need)
-        return TGEMM_ERROR_INVALID_VALUE;
-    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace);
-    if (workspace_bytes > UINTPTR_MAX - w0) return TGEMM_ERROR_INVALID_VALUE;
-    const uintptr_t w1 = w0 + workspace_bytes;
-    uintptr_t x0, x1;
-    if (span(A, ta ? K : M, ta ? M : K, lda, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
-    if (span(B, tb ? N : K, tb ? K : N, ldb, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
-    if (span(C, M, N, ldc, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
-    const bool vec4 = vec4_ok(ta, tb, M, N, K, A, lda, B, ldb);
-    const Split sp = choose_split(ta, tb, M, N, K, vec4, lda, ldb, splits);
-    if (sp.variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
-    if (sp.slices <= 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
-    float *W = static_cast<float *>(workspace);
-    GemmArgs g = pack(ta, tb, M, N, K, A, lda, B, ldb, W, N);
-    g.splits = sp.slices;
-    g.kchunk = sp.kchunk;
-    g.c_slice = M * N;
-    const tgemm::MfmaVariant *v = tgemm::mfma_variant(sp.variant);
-    const hipError_t e = v->launch(g, stream);
-    if (e != hipSuccess) return TGEMM_ERROR_HIP;
-    return from_hip(tgemm::launch_splitk_sum((int)M, (int)N, sp.slices, W, C, ldc, stream));
+    return splitk_launch(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspace_bytes, stream);
 }
 
 tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
@@ -349,6 +390,26 @@ tgemm_status_t tgemm_sgemm_splitk(int64_t M, int64_t N, int64_t K, const float *
 {
     return tgemm_sgemm_splitk_ex(TGEMM_OP_N, TGEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
                                  workspace_bytes, stream);
+}
+
+tgemm_status_t tgemm_sgemm_splitk_noalloc(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                                          const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                                          int64_t ldc, int splits, hipStream_t stream)
+{
+    if (!op_ok(op_a) || !op_ok(op_b)) return TGEMM_ERROR_NOT_SUPPORTED;
+    const bool ta = op_a == TGEMM_OP_T, tb = op_b == TGEMM_OP_T;
+    Quick quick;
+    const tgemm_status_t st = validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick);
+    if (st != TGEMM_SUCCESS) return st;
+    if (splits < 1 || splits > kMaxSplits) return TGEMM_ERROR_INVALID_VALUE;
+    if (quick == Quick::kDone) return TGEMM_SUCCESS;
+    if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
+    if (splits == 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    const size_t need = tgemm_sgemm_splitk_workspace_size(M, N, K, splits);
+    if (need == 0 || need > TGEMM_SPLITK_NOALLOC_BYTES) return TGEMM_ERROR_NOT_SUPPORTED;
+    void *ws = scratch_on_device();
+    if (ws == nullptr) return TGEMM_ERROR_HIP;
+    return splitk_launch(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, splits, ws, TGEMM_SPLITK_NOALLOC_BYTES, stream);
 }
 
 int tgemm_mfma_variant_count(void) { return tgemm::mfma_variant_count(); }
