@@ -117,8 +117,14 @@ def parse():
                    help="auto | naive | simt | lds<T>[p1] | mfma:<variant> | splitk[<slices>]")
     p.add_argument("--shape", default=None,
                    help="MxNxK: time a U[-1,1) product of that shape (seed 0) instead of --workload")
-    p.add_argument("--also", default="square4096_uniform",
+    p.add_argument("--also", default="square512_uniform,square1024_int4,square4096_uniform,rect3000x1000x5000_normal",
                    help="comma-separated extra workloads timed the same way ('' for none)")
+    p.add_argument("--small-steps", type=int, default=500,
+                   help="timed calls for the launch-bound workloads (512^3, 1024^3)")
+    p.add_argument("--ragged-steps", type=int, default=50, help="timed calls for 3000x1000x5000")
+    p.add_argument("--cold-also", default="square512_uniform,square1024_int4,square4096_uniform",
+                   help="workloads also timed with cold caches under 'cold' ('' for none)")
+    p.add_argument("--cold-steps", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-vendor", action="store_true",
                    help="skip timing the vendor BLAS (torch.matmul, fp32) beside the product")
@@ -153,7 +159,28 @@ def kernel_call(name: str):
     import tiled_gemm_tgemm_amd as tg
 
     if name == "auto":
-        return (lambda A, B, C: tg.sgemm(A, B, out=C)), "tgemm_sgemm"
+        # the C entry point itself, its arguments marshalled once per set of
+        # tensors (the Python wrapper's checks cost more than a 512^3 call)
+        lib = tg.library()
+        cache = {}
+
+        def call(A, B, C):
+            key = (A.data_ptr(), B.data_ptr(), C.data_ptr())
+            if key not in cache:
+                import torch
+
+                op_a, lda = tg._layout(A, "A")
+                op_b, ldb = tg._layout(B, "B")
+                cache.clear()
+                cache[key] = (op_a, op_b, A.shape[0], B.shape[1], A.shape[1], A.data_ptr(), lda, B.data_ptr(),
+                              ldb, C.data_ptr(), max(C.stride(0), C.shape[1], 1),
+                              torch.cuda.current_stream(A.device).cuda_stream)
+            st = lib.tgemm_sgemm_ex(*cache[key])
+            if st != tg.TGEMM_SUCCESS:
+                raise tg.TgemmError(st, "tgemm_sgemm_ex")
+            return C
+
+        return call, "tgemm_sgemm"
     if name == "naive":
         return (lambda A, B, C: tg.sgemm(A, B, out=C, kernel="naive")), "tgemm_sgemm_naive"
     if name == "simt":
@@ -265,6 +292,18 @@ def engine_clock(m, kernel: str, load_seconds: float = 2.0):
     exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
     if exe is None:
         return None
+    # amd-smi is a Python script started through "#!/usr/bin/env python3";
+    # run it with this interpreter directly, as a child process, so that no
+    # launcher replaces one program with another on the way
+    cmd = [exe]
+    real = os.path.realpath(exe)
+    try:
+        with open(real, "rb") as f:
+            first = f.readline()
+        if first.startswith(b"#!") and b"python" in first:
+            cmd = [sys.executable, real]
+    except OSError:
+        pass
     call, _ = kernel_call(kernel)
     A, B, C = m["A"], m["B"], m["C"]
     n = 0
@@ -282,7 +321,7 @@ def engine_clock(m, kernel: str, load_seconds: float = 2.0):
     busy_until(lambda: time.perf_counter() - t_load >= load_seconds)
     reading = None
     for _ in range(2):
-        child = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
+        child = subprocess.Popen(cmd + ["metric", "-c", "--json"], stdout=subprocess.PIPE,
                                  stderr=subprocess.DEVNULL, text=True)
         busy_until(lambda: child.poll() is not None)
         try:
@@ -347,17 +386,39 @@ def vendor_blas(m, steps: int, warmup_seconds: float):
 
 
 def traffic_for(workload_name: str, variant: str):
-    """Measured HBM bytes per launch from the committed counter summary, or None."""
+    """Measured HBM bytes per launch from the committed counter record, or
+    None: the record holds, per workload, the configuration it was taken on,
+    and the hash of the product kernel's code when it was taken."""
     if not os.path.exists(TRAFFIC_RECORD):
         return None
     with open(TRAFFIC_RECORD) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("kernel") != variant:
-        return None  # the kernel changed since the counters were taken, or another one runs
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
     entry = rec.get("workloads", {}).get(workload_name)
-    if not entry:
-        return None
+    if not entry or entry.get("kernel") != variant:
+        return None  # not measured, or on another configuration
     return entry.get("hbm_bytes_per_launch")
+
+
+def error_ratios(C, P, S, K: int):
+    """Rounding diagnostics of a real-valued product against the oracle's
+    float64 P and S = sum_k |a_ik b_kj|: max |dC| / (K 2^-24 S) (the
+    acceptance bound is 4), its RMS, and the RMS of dC / (sqrt(K) 2^-24 S),
+    which takes out the growth with K that independent roundings give."""
+    import numpy as np
+
+    d = np.abs(np.asarray(C, np.float64) - P)
+    u = 2.0 ** -24
+    pos = S > 0
+    if not np.all(d[~pos] == 0):
+        return {"max_ratio": float("inf"), "within_bound": False}
+    r = d[pos] / (K * u * S[pos])
+    r_sqrt = d[pos] / (np.sqrt(K) * u * S[pos])
+    return {"max_ratio": round(float(r.max()), 4) if r.size else 0.0,
+            "rms_ratio": round(float(np.sqrt(np.mean(r * r))), 5) if r.size else 0.0,
+            "rms_ratio_sqrt_k": round(float(np.sqrt(np.mean(r_sqrt * r_sqrt))), 4) if r.size else 0.0,
+            "within_bound": bool(r.size == 0 or r.max() <= 4.0)}
 
 
 def transpose_traffic_for(workload_name: str, kernel: str):
@@ -373,9 +434,17 @@ def transpose_traffic_for(workload_name: str, kernel: str):
     return entry.get("hbm_bytes_per_launch") if entry else None
 
 
-def cpu_baseline(m, target_s: float):
-    """The oracle on whole rows of the same product, sized to ~target_s."""
+def cpu_baseline(m, target_s: float, others=(), one_thread_workload=None):
+    """The oracle (float64 sums of exact float32 products, plus the sums of
+    |products|) timed on this host's cores.  `value`: whole rows of the
+    headline product, grown to ~target_s.  `full_oracle`: the whole product
+    of each workload in `others` (name -> (A, B, GPU result on the host)),
+    timed, and the GPU result checked against it (exact equality on integer
+    inputs, else the rounding diagnostics); then an extrapolated time for the
+    whole headline product at the largest of those products' oracle rate,
+    and the one-thread rate on `one_thread_workload`."""
     import numpy as np
+    import torch
 
     import oracle
 
@@ -393,14 +462,54 @@ def cpu_baseline(m, target_s: float):
         rows = min(w.M, int(rows * grow))
     macs = rows * w.N * w.K
     C_rows = m["C"][:rows].cpu().numpy().astype(np.float64)
-    ok = bool(np.all(np.abs(C_rows - P) <= 4.0 * w.K * 2.0 ** -24 * S))
-    return {
+    out = {
         "value": 2.0 * macs / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"first {rows} rows of C ({rows}x{w.N}, K={w.K}) of {w.name}: float64 sums "
                   f"with exact float32 products, plus the sums of |products|; {t:.2f} s",
-        "sample_rows_within_bound": ok,
+        "sample_rows_within_bound": bool(np.all(np.abs(C_rows - P) <= 4.0 * w.K * 2.0 ** -24 * S)),
+        "sample_rows_error": error_ratios(C_rows, P, S, w.K),
     }
+    full = {}
+    best_rate = None
+    for name, (wo, Ah, Bh, Ch) in others.items():
+        t0 = time.perf_counter()
+        P, S = oracle.gemm(Ah, Bh)
+        t = time.perf_counter() - t0
+        entry = {"seconds": round(t, 3), "gflops": round(wo.flops / t / 1e9, 2)}
+        if wo.dist == "int4":
+            t0 = time.perf_counter()
+            Pi = oracle.gemm_i64(Ah, Bh)
+            entry["int64_seconds"] = round(time.perf_counter() - t0, 3)
+            entry["gpu_exact"] = bool(np.array_equal(Ch.astype(np.int64), Pi) and np.array_equal(P, Pi))
+        else:
+            entry["gpu_error"] = error_ratios(Ch, P, S, wo.K)
+        full[name] = entry
+        if best_rate is None or wo.flops > best_rate[1]:
+            best_rate = (wo.flops / t, wo.flops, name)
+        del P, S
+    if full:
+        out["full_oracle"] = full
+        rate, _, name = best_rate
+        out["extrapolated_full_headline"] = {
+            "what": f"the whole {w.name} product by the oracle, extrapolated (not run) from the "
+                    f"{name} oracle rate: 2MNK / rate",
+            "seconds": round(w.flops / rate, 1)}
+    if one_thread_workload is not None:
+        wo, Ah, Bh = one_thread_workload
+        saved = torch.get_num_threads()
+        # the oracle's OpenMP regions share the runtime torch configured at import
+        torch.set_num_threads(1)
+        try:
+            t0 = time.perf_counter()
+            oracle.gemm(Ah, Bh)
+            t = time.perf_counter() - t0
+            threads = oracle.num_threads()
+        finally:
+            torch.set_num_threads(saved)
+        out["one_thread"] = {"workload": wo.name, "seconds": round(t, 3), "gflops": round(wo.flops / t / 1e9, 2),
+                             "threads": threads}
+    return out
 
 
 def time_transpose(w, kernel: str, steps: int, warmup: int, warmup_seconds: float):
@@ -601,6 +710,22 @@ def host_main(args, props):
     return 0
 
 
+def plain_also(args) -> bool:
+    """Whether the extra workloads run the default product (cold figures and
+    counter records belong to it)."""
+    return args.kernel == "auto" and args.op_a == "N" and args.op_b == "N" and not args.cold
+
+
+def steps_for(w, args) -> int:
+    """Timed calls for a workload: the launch-bound small products and the
+    ragged one get more, so their means rest on enough calls."""
+    if w.flops <= 2 * 1024 ** 3:
+        return max(args.steps, args.small_steps)
+    if w.name.startswith("rect"):
+        return max(args.steps, args.ragged_steps)
+    return args.steps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -682,21 +807,46 @@ def main():
     if vendor:
         line["vendor_blas"] = vendor_blas(m, args.steps, args.warmup_seconds)
     also = {}
+    others = {}  # inputs and GPU results kept for the oracle leg
+    cold_names = [x for x in args.cold_also.split(",") if x] if plain_also(args) else []
     for name in [x for x in args.also.split(",") if x and x != w.name]:
         wa = wl.WORKLOADS[name]
-        ma = time_workload(wa, args.kernel, args.steps, args.warmup, args.warmup_seconds, args.cold,
+        steps = steps_for(wa, args)
+        ma = time_workload(wa, args.kernel, steps, args.warmup, args.warmup_seconds, args.cold,
                            args.op_a, args.op_b)
-        also[name] = {
+        entry = {
             "tflops": round(ma["tflops_wall"], 3),
-            "ms_per_step": round(ma["wall_ms"], 4),
+            "ms_per_step": round(ma["wall_ms"], 5),
+            "steps": steps,
             "pct_of_fp32_matrix_peak": round(100.0 * ma["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2),
-            "kernel_ms_mean": round(ma["kernel_ms"], 4),
+            "kernel_ms_mean": round(ma["kernel_ms"], 5),
+            "kernel_ms_median": round(ma["kernel_ms_median"], 5),
             "roofline_frac": round(ma["tflops_kernel"] / PEAK_FP32_MATRIX_TFLOPS, 4),
             "algorithmic_hbm_gbs": round(wa.algorithmic_bytes / (ma["kernel_ms"] * 1e-3) / 1e9, 1),
+            "algorithmic_hbm_frac": round(wa.algorithmic_bytes / (ma["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
             "variant": ma["variant"],
         }
+        t_bytes = traffic_for(wa.name, ma["variant"]) if plain else None
+        if t_bytes:
+            gbs = t_bytes / (ma["kernel_ms"] * 1e-3) / 1e9
+            entry["measured_hbm"] = {"bytes_per_launch": t_bytes, "gbs": round(gbs, 1),
+                                     "frac_of_8tbs": round(gbs / PEAK_HBM_GBS, 5)}
         if vendor:
-            also[name]["vendor_blas"] = vendor_blas(ma, args.steps, args.warmup_seconds)
+            entry["vendor_blas"] = vendor_blas(ma, steps, args.warmup_seconds)
+        if name in cold_names:
+            mc = time_workload(wa, args.kernel, args.cold_steps, args.warmup, args.warmup_seconds, True,
+                               args.op_a, args.op_b)
+            entry["cold"] = {"what": "512 MiB written before every call (L2 and the Infinity Cache hold none "
+                                     "of the operands); kernel time",
+                             "steps": args.cold_steps, "kernel_ms_mean": round(mc["kernel_ms"], 5),
+                             "kernel_ms_median": round(mc["kernel_ms_median"], 5),
+                             "tflops": round(mc["tflops_kernel"], 3),
+                             "roofline_frac": round(mc["tflops_kernel"] / PEAK_FP32_MATRIX_TFLOPS, 4),
+                             "algorithmic_hbm_gbs": round(wa.algorithmic_bytes / (mc["kernel_ms"] * 1e-3) / 1e9, 1)}
+            del mc
+        also[name] = entry
+        if not args.no_cpu_baseline:
+            others[name] = (wa, ma["A_host"], ma["B_host"], ma["C"].cpu().numpy())
         del ma
     if also:
         line["also"] = also
@@ -714,7 +864,14 @@ def main():
             # the oracle's OpenMP regions share the runtime torch configured at
             # import; this sets the thread count they run with
             torch.set_num_threads(args.cpu_threads)
-        line["cpu_baseline"] = cpu_baseline(m, args.cpu_seconds)
+        one = None
+        if "square512_uniform" in others:
+            wo, Ah, Bh, _ = others["square512_uniform"]
+            one = (wo, Ah, Bh)
+        line["cpu_baseline"] = cpu_baseline(m, args.cpu_seconds, others, one)
+        # the GPU results of the other workloads against the whole oracle product
+        for name, entry in line["cpu_baseline"].get("full_oracle", {}).items():
+            also[name]["parity"] = {k: v for k, v in entry.items() if k in ("gpu_exact", "gpu_error")}
     print(json.dumps(line), flush=True)
     return 0
 

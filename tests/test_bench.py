@@ -38,8 +38,9 @@ def test_code_hash_ignores_comments_and_blank_lines(tmp_path):
 
 
 def test_traffic_record_is_used_only_for_the_kernel_it_was_taken_on(tmp_path, monkeypatch):
-    record = {"kernel_source_sha256": bench.kernel_source_hash(), "kernel": "m256n128k16_w2x2_vec4",
-              "workloads": {"square8192_uniform": {"hbm_bytes_per_launch": 123456789}}}
+    record = {"kernel_source_sha256": bench.kernel_source_hash(),
+              "workloads": {"square8192_uniform": {"kernel": "m256n128k16_w2x2_vec4",
+                                                   "hbm_bytes_per_launch": 123456789}}}
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(record))
     monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
@@ -85,3 +86,37 @@ def test_engine_clock_is_the_mean_over_the_xcds():
 ])
 def test_engine_clock_rejects_readings_it_cannot_trust(data):
     assert bench.mean_engine_clock(data) is None
+
+
+def test_error_ratios_against_known_differences():
+    import numpy as np
+
+    K = 1000
+    S = np.full((2, 3), 8.0)
+    P = np.zeros((2, 3))
+    u = 2.0 ** -24
+    C = np.array([[0.0, K * u * 8.0, -2 * K * u * 8.0], [0.5 * K * u * 8.0, 0.0, 0.0]])
+    r = bench.error_ratios(C, P, S, K)
+    assert r["max_ratio"] == 2.0 and r["within_bound"]
+    assert abs(r["rms_ratio"] - np.sqrt((1 + 4 + 0.25) / 6)) < 1e-4
+    assert abs(r["rms_ratio_sqrt_k"] - np.sqrt(K) * np.sqrt((1 + 4 + 0.25) / 6)) < 1e-2
+    C[0, 0] = 5 * K * u * 8.0
+    assert not bench.error_ratios(C, P, S, K)["within_bound"]
+    # where S is zero the product must be exactly zero
+    S[1, 1] = 0.0
+    C[0, 0] = 0.0
+    C[1, 1] = 1e-30
+    assert bench.error_ratios(C, P, S, K)["within_bound"] is False
+
+
+def test_step_counts_per_workload():
+    from tiled_gemm_tgemm_amd import workloads as wl
+
+    class A:  # noqa: N801 - the three options steps_for reads
+        steps, small_steps, ragged_steps = 20, 500, 50
+    W = wl.WORKLOADS
+    assert bench.steps_for(W["square512_uniform"], A) == 500
+    assert bench.steps_for(W["square1024_int4"], A) == 500
+    assert bench.steps_for(W["rect3000x1000x5000_normal"], A) == 50
+    assert bench.steps_for(W["square4096_uniform"], A) == 20
+    assert bench.steps_for(W["square8192_uniform"], A) == 20

@@ -224,6 +224,39 @@ def test_splitk_two_streams_two_workspaces():
         assert_exact(outs[1].cpu().numpy(), oracle.gemm_i64(A2, B2), f"stream 2, rep {rep}")
 
 
+def test_splitk_side_stream_internal_workspace_not_reused_early():
+    """sgemm_splitk on a side stream with no workspace given: the workspace
+    it allocates is released when it returns, while the side stream may
+    still be using it.  Allocations of the same size on the current stream
+    right after, each written at once, must not be handed that memory before
+    the side stream's work ends (the binding records the side stream on the
+    tensors it allocates); otherwise they overwrite partial products."""
+    M, N, K = 512, 512, 16384
+    A, B, _ = wl.random_matrices(M, N, K, "int4", 50)
+    dA, dB = dev(A), dev(B)
+    need = tg.tgemm_sgemm_splitk_workspace_size(M, N, K, 16)
+    side = torch.cuda.Stream()
+    X = torch.rand(4096, 4096, device="cuda")
+    Y = torch.empty_like(X)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        log(f"splitk side stream, internal workspace, rep {rep}")
+        # queue a few milliseconds of other work first, so that the split-K
+        # kernels are still pending when this thread returns and reallocates
+        for _ in range(3):
+            tg.sgemm(X, X, out=Y, stream=side.cuda_stream)
+        C = tg.sgemm_splitk(dA, dB, splits=16, stream=side.cuda_stream)
+        junk = []
+        for _ in range(24):
+            t = torch.empty(need, dtype=torch.uint8, device="cuda")
+            t.fill_(0xFF)  # NaN bit patterns, on the current stream
+            junk.append(t)
+            del junk[0:len(junk) - 2]
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), oracle.gemm_i64(A, B), f"side stream rep {rep}")
+        del C, junk
+
+
 @pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)])
 @pytest.mark.parametrize("M,N,K,splits", [(96, 80, 2048, 8), (65, 33, 3000, 4), (256, 256, 16384, None)])
 def test_splitk_transposed_operands_integer_exact(ta, tb, M, N, K, splits):

@@ -73,6 +73,22 @@ def _layout(t, name):
     raise ValueError(f"{name} must be row-major or a transposed row-major view")
 
 
+def _hold_for_stream(stream, device, *tensors):
+    """Tensors allocated here (on torch's current stream) but used by work
+    queued on another `stream`: record that stream on them, so that torch's
+    caching allocator does not hand their memory out again, once they are
+    released, before the work queued on `stream` so far has finished."""
+    import torch
+
+    if stream is None or not tensors:
+        return
+    if int(stream) == int(torch.cuda.current_stream(device).cuda_stream):
+        return
+    other = torch.cuda.ExternalStream(stream, device=device)
+    for t in tensors:
+        t.record_stream(other)
+
+
 def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream=None):
     """C = A·B for float32 CUDA tensors.
 
@@ -95,8 +111,10 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
         raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     op_a, lda = _layout(A, "A")
     op_b, ldb = _layout(B, "B")
+    made = []
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        made.append(out)
     else:
         out = _check(out, "out")
         if tuple(out.shape) != (M, N):
@@ -106,6 +124,7 @@ def sgemm(A, B, out=None, *, kernel="auto", variant=None, tile=16, pad=1, stream
     ldc = max(out.stride(0), N, 1)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
+    _hold_for_stream(stream, A.device, *made)
     args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc)
     if kernel in ("naive", "lds", "simt") and (op_a, op_b) != (TGEMM_OP_N, TGEMM_OP_N):
         raise ValueError(f"the {kernel} kernel takes row-major operands only")
@@ -145,8 +164,10 @@ def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
         raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     op_a, lda = _layout(A, "A")
     op_b, ldb = _layout(B, "B")
+    made = []
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        made.append(out)
     else:
         out = _check(out, "out")
         if tuple(out.shape) != (M, N):
@@ -159,10 +180,13 @@ def sgemm_splitk(A, B, out=None, *, splits=None, workspace=None, stream=None):
     need = tgemm_sgemm_splitk_workspace_size(M, N, K, splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A.device)
+        made.append(workspace)
     elif not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.dtype != torch.uint8:
         raise TypeError("workspace must be a CUDA uint8 tensor")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
+    # the workspace is released on return while the work on `stream` may still run
+    _hold_for_stream(stream, A.device, *made)
     st = tgemm_sgemm_splitk_ex(op_a, op_b, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc,
                                splits, workspace.data_ptr(), workspace.numel(), stream)
     if st != TGEMM_SUCCESS:
