@@ -168,11 +168,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const float *base, int6
 //   MC: mn-contiguous (B as stored, A transposed): element (mn, k) at
 //       ptr[k*ld + mn]; LDS keeps [k][mn], row stride MN+8.
 // Each thread owns L slots of VEC consecutive elements along the contiguous
-// dimension; consecutive threads own consecutive slots of a row, and one pass
-// of all threads covers R whole rows.  When R does not divide the slice's
-// rows (PART: a 160-row slice is 2.5 passes of 64), the last pass covers only
-// the threads whose row lies inside the slice; for the others that slot reads
-// nothing (offset past every extent) and is not written to LDS.
+// dimension; consecutive threads own consecutive slots of a row.
 template <bool KC_, int MN, int BK, int VEC, int NT>
 struct Loader {
     static constexpr bool KC = KC_;
@@ -180,16 +176,14 @@ struct Loader {
     static constexpr int COLS = KC ? BK : MN;           // contiguous extent of a row
     static constexpr int S = KC ? BK + 4 : MN + 8;      // LDS row stride (words)
     static constexpr int WORDS = ROWS * S;              // one LDS stage
+    static constexpr int L = ROWS * COLS / (VEC * NT);  // slots per thread
     static constexpr int R = NT * VEC / COLS;           // rows between a thread's slots
-    static constexpr int L = (ROWS + R - 1) / R;        // slots per thread
-    static constexpr bool PART = L * R != ROWS;         // the last pass is partial
-    static_assert((NT * VEC) % COLS == 0 && R >= 1 && L >= 1, "a pass of all threads covers whole rows");
+    static_assert((NT * VEC) % COLS == 0 && L >= 1 && L * R == ROWS, "slice splits into whole rows");
 
     typedef typename Vec<VEC>::type vec_t;
     uint32_t off[L];  // byte offset of each slot from the slice's first element
     int c;            // contiguous coordinate of the thread's slots
     int st;           // LDS word offset of slot 0 (slot i adds i*R*S)
-    bool last_in;     // (PART) the thread's last slot lies inside the slice
     vec_t reg[L];
 
     // mn_valid: rows (KC) or columns (MC) of this tile inside the matrix.
@@ -197,11 +191,10 @@ struct Loader {
     {
         const int r0 = t * VEC / COLS;
         c = t * VEC % COLS;
-        last_in = !PART || r0 + (L - 1) * R < ROWS;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int r = r0 + i * R;
-            const bool in = (KC ? r < mn_valid : c < mn_valid) && (i < L - 1 || last_in);
+            const bool in = KC ? r < mn_valid : c < mn_valid;
             off[i] = in ? (uint32_t)((r * ld + c) * 4) : kOutside;
         }
         st = r0 * S + c;
@@ -242,8 +235,7 @@ struct Loader {
     __device__ __forceinline__ void store(float *stage) const
     {
 #pragma unroll
-        for (int i = 0; i < L; ++i)
-            if (!PART || i < L - 1 || last_in) *reinterpret_cast<vec_t *>(stage + st + i * R * S) = reg[i];
+        for (int i = 0; i < L; ++i) *reinterpret_cast<vec_t *>(stage + st + i * R * S) = reg[i];
     }
 };
 
@@ -647,8 +639,9 @@ typedef Shape<256, 128, 16, 4, 4, 2, 1, 2, 2, 1> Large4;  // Aᵀ·B: one regist
 // one wavefront per SIMD holding a 128×128 sub-tile (512 registers)
 typedef Shape<256, 256, 16, 4, 4, 1> Huge4;
 typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
-// 160 rows of A as stored (2.5 passes of 64); four wavefronts side by side, each 160×32
-typedef Shape<160, 128, 16, 4, 4, 2, 1, 2, 1, 2, 4, false> Wide4;
+// 160 rows of A as stored (5 passes of 32 at 32 values of k); four wavefronts
+// side by side, each 160×32
+typedef Shape<160, 128, 32, 4, 4, 2, 1, 2, 1, 2, 4, false> Wide4;
 typedef Shape<64, 64, 32, 4, 8, 4> Small4;
 typedef Shape<256, 128, 16, 1, 4, 2, 1, 1> Large1;  // one register set (two spill)
 typedef Shape<128, 128, 32, 1, 8, 2> Mid1;
@@ -684,20 +677,24 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 // work-group per CU leaves its pipeline fill uncovered.  256×128 with A
 // transposed keeps one register set of staged loads (two spill) and runs
 // 3% slower than as stored (tn 0.969: 148.2 against 153.0 TFLOP/s at 8192³),
-// so Aᵀ·B goes to the 256×256 tile (153.0).  The 160×128 tile sustains less
-// (0.89 alone, 0.93 full) but spreads 3000×1000×5000 over three rounds of
-// tiles instead of one of 256×128 tiles (at most three of 160×128 per CU:
-// 60 blocks of 32×32 against 64), 228 against 235 µs.  The 4-byte-load
+// so Aᵀ·B goes to the 256×256 tile (153.0).  The 160×128 tile spreads
+// 3000×1000×5000 over three rounds of tiles instead of one of 256×128 tiles
+// (at most three of 160×128 per CU: 60 blocks of 32×32 against 64) and
+// leaves 248 tiles' stores exposed at the end instead of 480: 223.5 against
+// 234.6 µs.  Its phases hold 32 values of k (79 KB of LDS, still two
+// work-groups per CU): with 16 a phase is 2560 matrix-core cycles per
+// wavefront, and the tile sustained 0.88 alone and 0.92 full against 0.93
+// and 0.95 now (C4 228 µs).  The 4-byte-load
 // flavours keep their measured ratio to the 16-byte ones; the 32×32
 // K-split configurations were fitted to a sweep of 27 small, ragged, skinny
 // and long-K shapes with both load widths (one work-group per CU: 256 tiles
 // with K = 16384; CU full: 512 tiles with K = 4096 and 8192; the fixed cost
 // from 256³ and 512³).
 const MfmaVariant kVariants[] = {
-    TGEMM_VARIANT_TN("m256n128k16_w2x2_vec4", Large4, 0.977, 0.977, 7000.0, 0.969),
+    TGEMM_VARIANT_TN("m256n128k16_w2x2_vec4", Large4, 0.975, 0.977, 7000.0, 0.969),
     TGEMM_VARIANT("m256n256k16_w2x2_vec4", Huge4, 0.979, 0.979, 13000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.965, 0.965, 7000.0),
-    TGEMM_VARIANT("m160n128k16_w1x4_vec4_nn", Wide4, 0.8855, 0.9294, 7000.0),
+    TGEMM_VARIANT("m160n128k32_w1x4_vec4_nn", Wide4, 0.93, 0.95, 14000.0),
     TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.93, 7000.0),
     TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.937, 0.957, 7000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.844, 0.895, 7000.0),
