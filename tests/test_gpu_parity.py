@@ -19,6 +19,8 @@ times (tgemm_sgemm on contiguous operands).
 """
 
 import itertools
+import json
+import os
 import sys
 
 import numpy as np
@@ -68,7 +70,36 @@ def run(A, B, kernel="auto", **kw):
     return C.cpu().numpy()
 
 
-def assert_within_bound(C, P, S, K, what=""):
+# How much of the acceptance bound real-valued results use: a drift in the
+# kernels' accumulation order or rounding shows here long before it could
+# break the bound itself.  Above CANARY (a quarter of the worst case of
+# recursive float32 summation, K·2^-24·S) a test fails: the kernels measure
+# below 0.01 on every workload.
+CANARY = 0.25
+
+
+def error_stats(C, P, S, K):
+    """max and RMS over the elements of |C - P| / (K·2^-24·S); where S is
+    zero the element must be exactly zero (checked by the caller's bound)."""
+    err = np.abs(C.astype(np.float64) - P)
+    scale = K * TWO_M24 * S
+    pos = scale > 0
+    r = err[pos] / scale[pos]
+    if not r.size:
+        return 0.0, 0.0
+    return float(r.max()), float(np.sqrt(np.mean(r * r)))
+
+
+def record_error(what, K, mx, rms):
+    line = f"error ratio {what} (K={K}): max {mx:.5f} rms {rms:.6f} of K·2^-24·S"
+    log(line)
+    path = os.environ.get("TGEMM_ERROR_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"what": what, "K": K, "max_ratio": mx, "rms_ratio": rms}) + "\n")
+
+
+def assert_within_bound(C, P, S, K, what="", record=True):
     C = C.astype(np.float64)
     assert np.all(np.isfinite(C)), f"{what}: non-finite output"
     err = np.abs(C - P)
@@ -78,8 +109,11 @@ def assert_within_bound(C, P, S, K, what=""):
         i, j = np.argwhere(bad)[0]
         pytest.fail(f"{what}: {bad.sum()} elements outside the bound; first ({i},{j}): "
                     f"C={C[i, j]!r} P={P[i, j]!r} bound={bound[i, j]!r}")
-    ratio = float(np.max(err / np.maximum(K * TWO_M24 * S, 1e-300))) if err.size else 0.0
-    return ratio
+    mx, rms = error_stats(C, P, S, K)
+    if record:
+        record_error(what, K, mx, rms)
+    assert mx <= CANARY, f"{what}: max error ratio {mx} above the canary {CANARY}"
+    return mx
 
 
 def assert_exact(C, P_int, what=""):
@@ -124,10 +158,10 @@ def test_square512_uniform_all_kernels():
     P, S = oracle.gemm(A, B)
     fma = oracle.gemm_fma_f32(A, B)
     log(f"{w.name}: auto")
-    assert_within_bound(run(A, B), P, S, w.K, "auto")
+    assert_within_bound(run(A, B), P, S, w.K, f"{w.name} auto")
     for v, name in enumerate(variants()):
         log(f"{w.name}: {name}")
-        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, name)
+        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, f"{w.name} {name}")
     log(f"{w.name}: naive")
     C = run(A, B, "naive")
     assert np.array_equal(C, fma), "naive differs from the sequential fma model"
@@ -157,21 +191,44 @@ def test_square1024_int4_bit_exact():
     assert_exact(run(A, B, "simt"), Pi, "simt")
 
 
+# the pages' kernels and the vector-ALU one: (kernel, sgemm arguments)
+ABLATIONS = [("naive", {}), ("lds", dict(tile=16, pad=1)), ("lds", dict(tile=32, pad=0)), ("simt", {})]
+
+
 def test_rect3000x1000x5000_normal_masked_edges():
     w = wl.WORKLOADS["rect3000x1000x5000_normal"]
     A, B = wl.make_inputs(w)
     log(f"{w.name}: oracle")
     P, S = oracle.gemm(A, B)
-    log(f"{w.name}: auto")
-    assert_within_bound(run(A, B), P, S, w.K, "auto")
+    log(f"{w.name}: auto ({auto_variant(w.M, w.N, w.K)})")
+    assert_within_bound(run(A, B), P, S, w.K, f"{w.name} auto")
     for v, name in enumerate(variants()):
         log(f"{w.name}: {name}")
-        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, name)
+        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, f"{w.name} {name}")
+    # the ablation kernels through the full ragged shape (no dimension a
+    # multiple of any of their tiles): within the bound everywhere, and bit
+    # for bit the oracle's sequential float32 FMA model on the first rows and
+    # on the rows of the last, partial tile row
+    rows = np.r_[0:32, w.M - 40:w.M]
+    fma_rows = oracle.gemm_fma_f32(np.ascontiguousarray(A[rows]), B)
+    for kernel, kw in ABLATIONS:
+        name = kernel + "".join(f"{k}{v}" for k, v in kw.items())
+        log(f"{w.name}: {name}")
+        C = run(A, B, kernel, **kw)
+        assert_within_bound(C, P, S, w.K, f"{w.name} {name}")
+        assert np.array_equal(C[rows], fma_rows), f"{name} differs from the fma model on the sampled rows"
 
 
-def check_sampled(C, A, B, blocks, K, what):
-    for (r, c), (P, S) in zip(blocks, oracle.gemm_blocks(A, B, blocks, 64)):
-        assert_within_bound(C[r:r + 64, c:c + 64], P, S, K, f"{what} block ({r},{c})")
+def check_sampled(C, A, B, blocks, K, what, oracle_blocks=None):
+    oracle_blocks = oracle_blocks or oracle.gemm_blocks(A, B, blocks, 64)
+    for (r, c), (P, S) in zip(blocks, oracle_blocks):
+        assert_within_bound(C[r:r + 64, c:c + 64], P, S, K, f"{what} block ({r},{c})", record=False)
+    # the blocks' error ratios together
+    Cb = np.concatenate([C[r:r + 64, c:c + 64] for r, c in blocks])
+    Pb = np.concatenate([P for P, _ in oracle_blocks])
+    Sb = np.concatenate([S for _, S in oracle_blocks])
+    mx, rms = error_stats(Cb, Pb, Sb, K)
+    record_error(f"{what} ({len(blocks)} blocks of 64x64)", K, mx, rms)
     row, rowabs, col, colabs = oracle.checksums(A, B)
     C64 = C.astype(np.float64)
     M, N = C.shape
@@ -189,10 +246,14 @@ def test_square4096_uniform_full():
     A, B, blocks = wl.make_inputs_and_blocks(w)
     log(f"{w.name}: auto ({auto_variant(w.M, w.N, w.K)})")
     C = run(A, B)
-    check_sampled(C, A, B, blocks, w.K, w.name)
+    check_sampled(C, A, B, blocks, w.K, f"{w.name} auto")
     log(f"{w.name}: full oracle")
     P, S = oracle.gemm(A, B)
-    assert_within_bound(C, P, S, w.K, w.name)
+    assert_within_bound(C, P, S, w.K, f"{w.name} auto")
+    # every configuration against the whole product
+    for v, name in enumerate(variants()):
+        log(f"{w.name}: {name}")
+        assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, f"{w.name} {name}")
 
 
 def test_square8192_uniform_sampled():
@@ -200,7 +261,18 @@ def test_square8192_uniform_sampled():
     A, B, blocks = wl.make_inputs_and_blocks(w)
     log(f"{w.name}: auto ({auto_variant(w.M, w.N, w.K)})")
     C = run(A, B)
-    check_sampled(C, A, B, blocks, w.K, w.name)
+    ob = oracle.gemm_blocks(A, B, blocks, 64)
+    check_sampled(C, A, B, blocks, w.K, f"{w.name} auto", ob)
+    # every configuration on the same blocks (the checksums once, above)
+    for v, name in enumerate(variants()):
+        log(f"{w.name}: {name}")
+        C = run(A, B, "mfma", variant=v)
+        for (r, c), (P, S) in zip(blocks, ob):
+            assert_within_bound(C[r:r + 64, c:c + 64], P, S, w.K, f"{w.name} {name} block ({r},{c})",
+                                record=False)
+        Cb = np.concatenate([C[r:r + 64, c:c + 64] for r, c in blocks])
+        mx, rms = error_stats(Cb, np.concatenate([P for P, _ in ob]), np.concatenate([S for _, S in ob]), w.K)
+        record_error(f"{w.name} {name} ({len(blocks)} blocks of 64x64)", w.K, mx, rms)
 
 
 # ------------------------------------------------------------ edges, in integers

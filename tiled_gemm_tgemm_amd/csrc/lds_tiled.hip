@@ -11,12 +11,13 @@
 // another thread is still reading.  Each element read from device memory is
 // reused T times, so device reads drop from 2·N^3 to 2·N^3/T.
 //
-// Both tile copies are coalesced: consecutive tx read consecutive addresses of
+// Both tile copies are coalesced: consecutive lanes (lx) read consecutive addresses of
 // one A row and one B row (page 1, section [Coalescing], the tiled kernel's
 // two loads).  With PAD = 1 every tile row is one word longer, the
 // tile[32][33] idea of page 2 §1.4: on a 64-wide wavefront one wave spans
-// 64/T tile rows, so the A reads subM[ty][k] of different rows land T words
-// apart; the padding moves them to different banks.
+// 64/T tile rows, so its A reads (row ly, column k of the A slice) from
+// different rows land T words apart; the padding moves them to different
+// banks.
 //
 // Edges: the pages assume Width is a multiple of the tile.  Here rows, columns
 // and k beyond the matrix load as zero and are never stored, so any M, N, K
@@ -27,34 +28,61 @@
 namespace tgemm {
 namespace {
 
+// One operand's T×T slice of a phase in LDS (rows padded by PAD words), and
+// the thread's place in it.  fill_a / fill_b copy the thread's one element from
+// device memory, zero where it lies outside the operand.
+template <int T, int PAD>
+struct Stage {
+    float cell[T][T + PAD];
+
+    // A slice: the element (row, k0 + lane) of A, kept at [lane_y][lane_x]
+    __device__ __forceinline__ void fill_a(const float *a_row, bool row_ok, int k, int K, int ly, int lx)
+    {
+        cell[ly][lx] = (row_ok && k < K) ? a_row[k] : 0.0f;
+    }
+    // B slice: the element (k0 + lane_y, col) of B, kept at [lane_y][lane_x]
+    __device__ __forceinline__ void fill_b(const float *b_col, int64_t ldb, bool col_ok, int k, int K, int ly,
+                                           int lx)
+    {
+        cell[ly][lx] = (col_ok && k < K) ? b_col[(int64_t)k * ldb] : 0.0f;
+    }
+};
+
+// The thread's output summed over one phase: row ly of the A slice against
+// column lx of the B slice, one fused multiply-add per k in ascending order.
+template <int T, int PAD>
+__device__ __forceinline__ float dot_phase(const Stage<T, PAD> &a, const Stage<T, PAD> &b, int ly, int lx,
+                                           float acc)
+{
+#pragma unroll
+    for (int k = 0; k < T; ++k) acc = __builtin_fmaf(a.cell[ly][k], b.cell[k][lx], acc);
+    return acc;
+}
+
 template <int T, int PAD>
 __global__ __launch_bounds__(T *T) void lds_tiled_kernel(int M, int N, int K,
                                                          const float *__restrict__ A, int64_t lda,
                                                          const float *__restrict__ B, int64_t ldb,
                                                          float *__restrict__ C, int64_t ldc)
 {
-    __shared__ float subM[T][T + PAD];
-    __shared__ float subN[T][T + PAD];
+    __shared__ Stage<T, PAD> a_stage, b_stage;
 
-    const int tx = threadIdx.x, ty = threadIdx.y;
-    const int col = blockIdx.x * T + tx;
-    const int row = blockIdx.y * T + ty;
-    const bool row_in = row < M, col_in = col < N;
-    const float *a_row = A + (int64_t)(row_in ? row : 0) * lda;
-    const float *b_col = B + (col_in ? col : 0);
+    // the block's output tile and this thread's output in it (x along columns)
+    const int lx = threadIdx.x, ly = threadIdx.y;
+    const int out_row = blockIdx.y * T + ly, out_col = blockIdx.x * T + lx;
+    const bool row_ok = out_row < M, col_ok = out_col < N;
+    const float *a_row = A + (int64_t)(row_ok ? out_row : 0) * lda;
+    const float *b_col = B + (col_ok ? out_col : 0);
 
-    float pvalue = 0.0f;
-    const int phases = (K + T - 1) / T;
-    for (int m = 0; m < phases; ++m) {
-        const int ka = m * T + tx;  // column of A this thread copies
-        const int kb = m * T + ty;  // row of B this thread copies
-        subM[ty][tx] = (row_in && ka < K) ? a_row[ka] : 0.0f;
-        subN[ty][tx] = (col_in && kb < K) ? b_col[(int64_t)kb * ldb] : 0.0f;
-        __syncthreads();  // both tiles complete before anyone reads them
-        for (int k = 0; k < T; ++k) pvalue = __builtin_fmaf(subM[ty][k], subN[k][tx], pvalue);
-        __syncthreads();  // nobody reads the tiles any more before they are refilled
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += T) {
+        a_stage.fill_a(a_row, row_ok, k0 + lx, K, ly, lx);
+        b_stage.fill_b(b_col, ldb, col_ok, k0 + ly, K, ly, lx);
+        __syncthreads();  // both slices complete before any thread reads them
+        acc = dot_phase(a_stage, b_stage, ly, lx, acc);
+        __syncthreads();  // no thread still reads a slice when the next phase refills it
     }
-    if (row_in && col_in) C[(int64_t)row * ldc + col] = pvalue;
+    if (row_ok && col_ok) C[(int64_t)out_row * ldc + out_col] = acc;
 }
 
 template <int T, int PAD>

@@ -19,6 +19,16 @@ namespace {
 
 constexpr int kBlock = 16;
 
+// Row `a` of A against column `b` of B (stride ldb): one fused multiply-add
+// per k in ascending order, rounded once each.
+__device__ __forceinline__ float row_dot_column(const float *__restrict__ a, const float *__restrict__ b,
+                                                int64_t ldb, int K)
+{
+    float acc = 0.0f;
+    for (int k = 0; k < K; ++k, b += ldb) acc = __builtin_fmaf(a[k], *b, acc);
+    return acc;
+}
+
 __global__ __launch_bounds__(kBlock *kBlock) void naive_kernel(int M, int N, int K,
                                                                const float *__restrict__ A,
                                                                int64_t lda,
@@ -27,14 +37,10 @@ __global__ __launch_bounds__(kBlock *kBlock) void naive_kernel(int M, int N, int
                                                                float *__restrict__ C,
                                                                int64_t ldc)
 {
-    const int col = blockIdx.x * blockDim.x + threadIdx.x;
-    const int row = blockIdx.y * blockDim.y + threadIdx.y;
-    if (row >= M || col >= N) return;
-    const float *a = A + (int64_t)row * lda;
-    const float *b = B + col;
-    float value = 0.0f;
-    for (int k = 0; k < K; ++k) value = __builtin_fmaf(a[k], b[(int64_t)k * ldb], value);
-    C[(int64_t)row * ldc + col] = value;
+    // this thread's output: x along C's columns, y along its rows
+    const int i = blockIdx.y * kBlock + threadIdx.y;
+    const int j = blockIdx.x * kBlock + threadIdx.x;
+    if (i < M && j < N) C[(int64_t)i * ldc + j] = row_dot_column(A + (int64_t)i * lda, B + j, ldb, K);
 }
 
 }  // namespace
