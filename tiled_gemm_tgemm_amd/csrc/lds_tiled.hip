@@ -30,9 +30,11 @@ namespace {
 
 // One operand's T×T slice of a phase in LDS (rows padded by PAD words), and
 // the thread's place in it.  fill_a / fill_b copy the thread's one element from
-// device memory, zero where it lies outside the operand.
+// device memory, zero where it lies outside the operand.  Aligned to 16 bytes,
+// so that without padding a row's consecutive words can be read 16 bytes at a
+// time.
 template <int T, int PAD>
-struct Stage {
+struct alignas(16) Stage {
     float cell[T][T + PAD];
 
     // A slice: the element (row, k0 + lane) of A, kept at [lane_y][lane_x]
