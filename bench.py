@@ -3,8 +3,11 @@
 
 A step is one call of the product (tgemm_sgemm) on seeded synthetic inputs
 that are already resident in device memory.  Default workload: 8192³ with
-U[-1,1] inputs (seed 4); the 4096³ workload (seed 2) is timed the same way
-and reported alongside, since the headline metric covers both sizes.
+U[-1,1] inputs (seed 4).  The other four workloads (512³, 1024³ integers,
+4096³, 3000×1000×5000) are timed the same way and reported under "also",
+each with its own step count (--small-steps for the launch-bound two,
+--ragged-steps for the ragged one); the three smaller ones are timed again
+with cold caches under "cold".
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
                   [--kernel auto|naive|lds16|lds32|simt|mfma:<variant>]
