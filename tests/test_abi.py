@@ -196,8 +196,8 @@ def test_kernel_choice_checks(lib):
 def test_variant_choice(lib):
     names = tg.variant_names()
 
-    def chosen(M, N, K, a=1 << 40, lda=None, ldb=None, ldc=None):
-        v = tg.tgemm_sgemm_variant_for(M, N, K, a, lda or K, 1 << 44, ldb or N, 1 << 46, ldc or N)
+    def chosen(M, N, K, a=1 << 40, lda=None, ldb=None, ldc=None, c=1 << 46):
+        v = tg.tgemm_sgemm_variant_for(M, N, K, a, lda or K, 1 << 44, ldb or N, c, ldc or N)
         return names[v] if v >= 0 else None
 
     # MI355X: 8192³ 7.16-7.20 ms (256×256) against 7.18-7.19 (256×128) with 24%
@@ -208,6 +208,10 @@ def test_variant_choice(lib):
     assert chosen(8192, 4096, 1024) == "m256n128k16_w2x2_vec4"    # 472 µs against 477
     # ragged: three rounds of 160×128 tiles, 223.5 µs against 234.6 for one of 256×128
     assert chosen(3000, 5000, 1000) == "m160n128k32_w1x4_vec4_nn"
+    # that tile stores C four columns at a time: not chosen when C's rows are
+    # not 16-byte aligned (it would store one element at a time)
+    assert chosen(3000, 5000, 1000, c=(1 << 46) + 4) != "m160n128k32_w1x4_vec4_nn"
+    assert chosen(3000, 5000, 1000, ldc=5001) != "m160n128k32_w1x4_vec4_nn"
     assert chosen(640, 8192, 1000) == "m64n64k32_w2x2_vec4"       # 79.1 µs against 79.8 for 160×128
     # 32×32 tiles with K split over eight wavefronts: 7.3-7.5 µs against 11.7
     # for 64×64 tiles on MI355X

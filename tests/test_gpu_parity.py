@@ -349,6 +349,32 @@ def test_guard_bands(M, N, K, pad):
         assert np.all(big[outside] == 12345.0), f"{kernel} {kw} wrote outside C"
 
 
+@pytest.mark.parametrize("shift,extra", [(0, 0), (0, 1), (1, 3), (2, 4)])
+def test_row_store_epilogue_any_c_alignment(shift, extra):
+    """The 160×128 tile forms its blocks transposed and stores C four columns
+    at a time when C's rows are 16-byte aligned, one element at a time
+    otherwise.  C placed `shift` words into a sentinel buffer whose rows are
+    N + extra words apart: every placement gives the exact product and
+    writes nothing outside C (page 1, section [Matrix Multiplication]: each
+    output written once, where it belongs)."""
+    M, N, K = 333, 260, 100
+    A, B = int_inputs(M, N, K, 77 + shift + extra)
+    Pi = oracle.gemm_i64(A, B)
+    name = "m160n128k32_w1x4_vec4_nn"
+    v = variants().index(name)
+    rows, cols = M + 2, N + extra + shift
+    big = torch.full((rows, cols), 12345.0, dtype=torch.float32, device="cuda")
+    Cv = big[:M, shift:shift + N]
+    log(f"row-store epilogue {M}x{N}x{K} shift {shift} extra {extra}: {name}")
+    tg.sgemm(dev(A), dev(B), out=Cv, kernel="mfma", variant=v)
+    torch.cuda.synchronize()
+    got = big.cpu().numpy()
+    assert_exact(got[:M, shift:shift + N], Pi, f"{name} shift {shift} extra {extra}")
+    outside = np.ones(got.shape, bool)
+    outside[:M, shift:shift + N] = False
+    assert np.all(got[outside] == 12345.0), f"{name} wrote outside C"
+
+
 @pytest.mark.parametrize("K", [1, 4, 15, 16, 17, 20, 31, 32, 33, 36, 48, 64, 100])
 def test_partial_phases_integer_exact(K):
     """K below, at and just past the phase depths (16 and 32) of every

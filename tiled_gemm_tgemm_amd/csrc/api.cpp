@@ -182,12 +182,12 @@ double sum_cycles(int64_t M, int64_t N, int slices)
 
 // Best configuration for exactly up to `splits` slices (splits >= 2).
 Split choose_split(bool ta, bool tb, int64_t M, int64_t N, int64_t K, bool vec4, int64_t lda, int64_t ldb,
-                   int splits)
+                   int splits, bool c16)
 {
     Split best;
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
-        if (!v->split_k || !runs(*v, vec4, ta, tb, lda, ldb)) continue;
+        if (!v->split_k || !runs(*v, vec4, ta, tb, lda, ldb) || (v->c16 && !c16)) continue;
         const int64_t kc = kchunk_for(*v, K, splits);
         const int64_t slices = (K + kc - 1) / kc;
         const int64_t tiles = ((M + v->bm - 1) / v->bm) * ((N + v->bn - 1) / v->bn);
@@ -207,14 +207,15 @@ constexpr int kMaxSplits = 64;
 constexpr int64_t kMinSliceK = 1024;
 
 int choose_variant(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
-                   const float *B, int64_t ldb)
+                   const float *B, int64_t ldb, const float *C, int64_t ldc)
 {
+    const bool c16 = aligned16(C) && ldc % 4 == 0;
     const bool vec4 = vec4_ok(ta, tb, M, N, K, A, lda, B, ldb);
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < tgemm::mfma_variant_count(); ++i) {
         const tgemm::MfmaVariant *v = tgemm::mfma_variant(i);
-        if (!runs(*v, vec4, ta, tb, lda, ldb)) continue;
+        if (!runs(*v, vec4, ta, tb, lda, ldb) || (v->c16 && !c16)) continue;
         const double c = cost(*v, ta, tb, M, N, K);
         if (best < 0 || c < best_cost) {
             best = i;
@@ -243,7 +244,8 @@ tgemm_status_t splitk_launch(bool ta, bool tb, int64_t M, int64_t N, int64_t K, 
     if (span(B, tb ? N : K, tb ? K : N, ldb, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
     if (span(C, M, N, ldc, x0, x1) && overlaps(w0, w1, x0, x1)) return TGEMM_ERROR_INVALID_VALUE;
     const bool vec4 = vec4_ok(ta, tb, M, N, K, A, lda, B, ldb);
-    const Split sp = choose_split(ta, tb, M, N, K, vec4, lda, ldb, splits);
+    // the slices go to the workspace (16-byte aligned, rows of N floats)
+    const Split sp = choose_split(ta, tb, M, N, K, vec4, lda, ldb, splits, N % 4 == 0);
     if (sp.variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
     if (sp.slices <= 1) return tgemm_sgemm_ex(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, stream);
     float *W = static_cast<float *>(workspace);
@@ -323,7 +325,7 @@ tgemm_status_t tgemm_sgemm_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int64
     const tgemm_status_t st = validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick);
     if (st != TGEMM_SUCCESS || quick == Quick::kDone) return st;
     if (quick == Quick::kZeroFill) return from_hip(tgemm::launch_fill_zero((int)M, (int)N, C, ldc, stream));
-    const int variant = choose_variant(ta, tb, M, N, K, A, lda, B, ldb);
+    const int variant = choose_variant(ta, tb, M, N, K, A, lda, B, ldb, C, ldc);
     if (variant < 0) return TGEMM_ERROR_NOT_SUPPORTED;
     return from_hip(tgemm::mfma_variant(variant)->launch(pack(ta, tb, M, N, K, A, lda, B, ldb, C, ldc), stream));
 }
@@ -358,7 +360,7 @@ int tgemm_sgemm_splitk_choose(int64_t M, int64_t N, int64_t K)
     // 384×640×4096, 23.7 µs with 4 slices against 30.4 with 16)
     int pick = 1;
     for (int splits = 2; splits <= kMaxSplits && (K + splits - 1) / splits >= kMinSliceK; splits *= 2) {
-        const Split sp = choose_split(false, false, M, N, K, true, max1(K), max1(N), splits);
+        const Split sp = choose_split(false, false, M, N, K, true, max1(K), max1(N), splits, true);
         if (sp.variant >= 0 && sp.slices > 1 && (best < 0 || sp.cycles < best)) {
             best = sp.cycles;
             pick = splits;
@@ -429,7 +431,7 @@ int tgemm_sgemm_variant_for_ex(tgemm_op_t op_a, tgemm_op_t op_b, int64_t M, int6
     Quick quick;
     if (validate(ta, tb, M, N, K, A, lda, B, ldb, C, ldc, quick) != TGEMM_SUCCESS || quick != Quick::kNone)
         return -1;
-    return choose_variant(ta, tb, M, N, K, A, lda, B, ldb);
+    return choose_variant(ta, tb, M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 int tgemm_sgemm_variant_for(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,

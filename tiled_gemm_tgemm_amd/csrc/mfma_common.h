@@ -101,6 +101,22 @@ __device__ __forceinline__ void mfma_group(f32x16 (&acc)[FM][FN], const Frag &f)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[j][s], acc[i][j], 0, 0, 0);
 }
 
+// The same steps with the operands exchanged: the matrix core then forms
+// the transpose of each 32×32 block, so that a lane holds four consecutive
+// columns of one row of C (store_c_t) instead of four rows of one column.
+// The products and the order in which they are added are the same.
+template <int FM, int FN, class Frag>
+__device__ __forceinline__ void mfma_group_t(f32x16 (&acc)[FM][FN], const Frag &f)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.b[j][s], f.a[i][s], acc[i][j], 0, 0, 0);
+}
+
 // Word offset of this lane's fragment of block `blk` (32 rows of A or 32
 // columns of B, counted from the wavefront's first) for k-group g, in a
 // slice kept KC ([mn][k], row stride S) or MC ([k][mn], row stride S).
@@ -166,6 +182,39 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[FM][FN], float *__re
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
                 if (row < M) c[(int64_t)row * ldc] = acc[i][j][r];
+            }
+    }
+}
+
+// The epilogue for blocks formed by mfma_group_t: accumulator r of lane (l32,
+// half) in block (i, j) is C row i*32 + l32, column j*32 + 8*(r/4) + 4*half +
+// r%4.  With `vec` (C and its leading dimension 16-byte aligned) each group
+// of four columns inside C is one 16-byte store; otherwise, and at the last
+// columns, one store per element.  Rows >= M and columns >= N are not written.
+template <int FM, int FN>
+__device__ __forceinline__ void store_c_t(const f32x16 (&acc)[FM][FN], float *__restrict__ C, int64_t ldc,
+                                          int M, int N, int row0, int col0, int half, int l32, bool vec)
+{
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = row0 + i * 32 + l32;
+        if (row >= M) continue;
+        float *c = C + (int64_t)row * ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = col0 + j * 32 + 8 * q + 4 * half;
+                if (vec && col + 3 < N) {
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+                    *reinterpret_cast<f32x4 *>(c + col) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < N) c[col + e] = acc[i][j][4 * q + e];
+                }
             }
     }
 }

@@ -81,6 +81,10 @@ struct MfmaVariant {
     // measured rate with A stored transposed and B as stored, relative to
     // operands as stored (used only to rank configurations)
     double tn_factor = 1.0;
+    // forms its blocks transposed and stores C four columns at a time: chosen
+    // by the cost model only when C and its leading dimension are 16-byte
+    // aligned (it runs on any C, one store per element otherwise)
+    bool c16 = false;
 };
 
 // Tiled buffer-load kernels (mfma_sgemm.hip) and the 64-bit-pointer fallback
