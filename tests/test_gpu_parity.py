@@ -205,6 +205,27 @@ def test_rect3000x1000x5000_normal_masked_edges():
     for v, name in enumerate(variants()):
         log(f"{w.name}: {name}")
         assert_within_bound(run(A, B, "mfma", variant=v), P, S, w.K, f"{w.name} {name}")
+    # C's rows one word off 16-byte alignment: the automatic choice leaves the
+    # 160×128 tile (whose epilogue writes 16-byte row pieces), and that tile
+    # run explicitly stores element by element, with the same bits as its
+    # aligned run
+    row_store = "m160n128k32_w1x4_vec4_nn"
+    big = torch.full((w.M, w.N + 1), float("nan"), dtype=torch.float32, device="cuda")
+    Cv = big[:, 1:]
+    Ad, Bd = dev(A), dev(B)
+    chosen = tg.tgemm_sgemm_variant_for(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N,
+                                        Cv.data_ptr(), w.N + 1)
+    log(f"{w.name}: auto into unaligned C ({variants()[chosen]})")
+    assert variants()[chosen] != row_store
+    tg.sgemm(Ad, Bd, out=Cv)
+    torch.cuda.synchronize()
+    assert_within_bound(Cv.cpu().numpy(), P, S, w.K, f"{w.name} auto, unaligned C", record=False)
+    log(f"{w.name}: {row_store} into unaligned C")
+    tg.sgemm(Ad, Bd, out=Cv, kernel="mfma", variant=variants().index(row_store))
+    torch.cuda.synchronize()
+    assert np.array_equal(Cv.cpu().numpy(), run(A, B, "mfma", variant=variants().index(row_store))), \
+        f"{row_store}: unaligned C differs from aligned C"
+    del big, Cv, Ad, Bd
     # the ablation kernels through the full ragged shape (no dimension a
     # multiple of any of their tiles): within the bound everywhere, and bit
     # for bit the oracle's sequential float32 FMA model on the first rows and

@@ -72,25 +72,21 @@
 //   8192³ with 4-byte loads forced: plain schedule 140.3 TFLOP/s,
 //   interleaved with one set 148.8, with two sets 134.3 (spilling); at
 //   128×128 two sets are ahead (139.3 against 133.3 plain).
-// * K split inside a work-group (64×64 tiles with KS = 2 or 4 groups of four
-//   wavefronts; 32×32 tiles with KS = 4 or 8 single wavefronts):
-//   on shapes with too few tiles to give every SIMD more than one wavefront
-//   (about 1024³, or small M·N with long K), the work-group holds KS groups
-//   of wavefronts, each running the pipeline above over its own slice of K
-//   (a whole number of phases; the last slice shorter) with its own LDS
-//   stages and registers.  Every slice runs the same phases, so the barriers
-//   stay uniform; reads past a slice's end return zero.  At the end the
-//   slices' sums meet in LDS and slice 0 adds them in slice order and writes
-//   C, so the result does not depend on timing.  Measured on MI355X:
-//   1024×1024×8192 210 → 156 µs, 1024³ 29 → 24 µs with four slices.  Since
-//   the whole-phase loads and the persistent grid, the unsplit 64×64 tile is
-//   ahead on every shape measured (1024×1024×8192: 133 against 148 µs;
-//   768×768×8192: 132 against 147 µs), so the selection model no longer
-//   picks the 64×64 splits; they stay available through tgemm_sgemm_mfma.
-//   With 32×32 tiles and one wavefront per slice the split is what fills
-//   the chip where even 64×64 tiles leave CUs idle (512³: 7.5 µs against
-//   10.3 for the small-product kernel; 512×512×16384: 94.8 against 156;
-//   2048×256×8192: 92.0 against 131 for 64×64).
+// * K split inside a work-group (32×32 tiles with KS = 4 or 8 single
+//   wavefronts): on shapes with too few tiles to give every SIMD a
+//   wavefront (M·N up to about 640², or skinny shapes with long K), the
+//   work-group holds KS groups of wavefronts, each running the pipeline
+//   above over its own slice of K (a whole number of phases; the last slice
+//   shorter) with its own LDS stages and registers.  Every slice runs the
+//   same phases, so the barriers stay uniform; reads past a slice's end
+//   return zero.  At the end the slices' sums meet in LDS and slice 0 adds
+//   them in slice order and writes C, so the result does not depend on
+//   timing.  Measured on MI355X (µs, against the best unsplit tile): 512³
+//   7.5 against 11.7; 512×512×16384 94.8 against 156; 2048×256×8192 92.0
+//   against 131.  The same split of 64×64 tiles into 2 or 4 groups of four
+//   wavefronts lost to the unsplit 64×64 tile once the loads below were
+//   whole-phase and the grid persistent (1024×1024×8192: 148 against 133),
+//   and is no longer built.
 // * K split across work-groups (gridDim.y > 1, from tgemm_sgemm_splitk):
 //   work-group (x, s) runs the whole pipeline above over the k range
 //   [s·kchunk, min(K, (s+1)·kchunk)) and writes its partial tiles to block s
