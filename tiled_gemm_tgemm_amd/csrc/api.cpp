@@ -98,6 +98,9 @@ bool vec4_ok(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float *A, 
 // 64-bit-pointer fallback takes operands as stored only.
 bool runs(const tgemm::MfmaVariant &v, bool vec4, bool ta, bool tb, int64_t lda, int64_t ldb)
 {
+    // a configuration whose work-group does not fit on a compute unit cannot
+    // run (and the cost model divides by work-groups per CU)
+    if (v.wg_per_cu < 1) return false;
     if ((ta || tb) && !v.trans) return false;
     return (v.vec == 1 || vec4) && lda <= (ta ? v.max_lda_t : v.max_lda) &&
            ldb <= (tb ? v.max_ldb_t : v.max_ldb);

@@ -612,8 +612,6 @@ struct Shape {
     using C = Cfg<BM, BN, BK, W, WN, VEC, GM, OCC, TA, TB, KS, (TA && !TB) ? NS_TN : NS, SWAPC>;
     static constexpr bool trans = TRANS;
     static constexpr bool c16 = SWAPC;
-    // the cost model divides by the work-groups a CU holds
-    static_assert(wg_per_cu<C<false, false>>() >= 1, "a work-group must fit on a compute unit");
     static hipError_t launch(const GemmArgs &g, hipStream_t stream)
     {
         if constexpr (!TRANS) {
