@@ -73,7 +73,7 @@ typedef enum tgemm_status {
  * tile by tile as in page 1's section [Shared Memory] and page 2 ("Lec 29 ·
  * GPU Architecture (2)") §1.2 — tiles of A and B staged through on-chip
  * memory in phases, one barrier per phase, sums kept in registers — with
- * the tile shape chosen from M, N, K and the operands' alignment.
+ * the tile shape chosen from M, N, K and the alignment of A, B and C.
  * Arguments and errors: see the conventions above.
  */
 tgemm_status_t tgemm_sgemm(int64_t M, int64_t N, int64_t K,
@@ -201,8 +201,10 @@ int tgemm_mfma_variant_count(void);
  * 256×128, depth 16 per phase, 2×2 wavefronts, 16-byte loads),
  * "m32n32k32_w1x1s8_vec4" (32×32 tile staged through LDS, K split over 8
  * single-wavefront slices), "..._nn" (operands as stored only: TGEMM_OP_T is
- * refused), "..._flat" (64-bit pointers, any leading dimension, operands as
- * stored only); NULL for an index out of range.
+ * refused; "m160n128k32_w1x4_vec4_nn" also writes C in 16-byte row pieces,
+ * so tgemm_sgemm picks it only when C and ldc are 16-byte aligned, though it
+ * runs on any C), "..._flat" (64-bit pointers, any leading dimension,
+ * operands as stored only); NULL for an index out of range.
  */
 const char *tgemm_mfma_variant_name(int variant);
 

@@ -142,8 +142,9 @@ double cost_tiles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t K, double 
 // 14 µs, the 64 MB of C; 16 values of k take 17.9 µs in all).  Earlier
 // rounds' stores overlap the next round's work in part, which the fixed cost
 // per round stands for.  This is what lets a tile that spreads a ragged shape
-// over more, shorter rounds win (3000×1000×5000: 160×128 tiles, the last of
-// three rounds 248 tiles, 228 µs; 256×128, one round of 480 tiles, 235 µs).
+// over more, shorter rounds win (3000×1000×5000: 760 tiles of 160×128, the
+// second and last round 248 of them, 219-222 µs; 480 tiles of 256×128, all in
+// one round, 234 µs).
 double final_store_cycles(const tgemm::MfmaVariant &v, int64_t tiles, int64_t M, int64_t N)
 {
     const int64_t slots = (int64_t)256 * v.wg_per_cu;
