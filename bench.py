@@ -31,9 +31,12 @@ calls (the GPU clock takes a few tens of milliseconds of load to settle).
 Reported:
 * value / ms_per_step — wall clock over the timed steps, between two device
   synchronisations, throughput = 2·M·N·K / time;
-* roofline — the product kernel's average duration from HIP events recorded
-  on the stream it is launched on, its algorithmic flops (2·M·N·K per
-  launch) over that time, against the MI355X dense fp32 matrix peak; the
+* roofline — the product kernel's average duration per launch, from one pair
+  of HIP events recorded around the timed steps on the stream they are
+  launched on, its algorithmic flops (2·M·N·K per launch) over that time,
+  against the MI355X dense fp32 matrix peak (kernel_ms also gives the
+  spread of single calls, each between its own events, from as many calls
+  after the timed region); the
   measured HBM traffic per launch comes from the committed rocprofv3 counter
   summary when it was taken on the current kernel source, else null;
 * engine_clock — the XCDs' mean engine clock read with amd-smi while the
@@ -253,26 +256,47 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
             torch.cuda.synchronize()
     stream = torch.cuda.current_stream()  # the stream every call is queued on
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda") if cold else None
-    t0 = time.perf_counter()
-    for i in range(steps):
-        if cold:
-            flush.fill_(float(i))
-        starts[i].record(stream)
-        call(A, B, C)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
-    # with --cold the wall clock also covers the flushes: report kernel time only
-    wall_ms = float(per.mean()) if cold else (t1 - t0) * 1e3 / steps
-    kernel_ms = float(per.mean())
+
+    def per_call_events(n, flush=None):
+        """n calls, each between its own pair of events (ms per call)."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(float(i))
+            starts[i].record(stream)
+            call(A, B, C)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    if cold:
+        # a 512 MiB fill before every call; the wall clock would cover the
+        # fills too, so the figure is the calls' own event time
+        flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        per = per_call_events(steps, flush)
+        wall_ms = kernel_ms = float(per.mean())
+    else:
+        # the timed region: `steps` calls back to back, one event pair on the
+        # calls' stream around all of them (events between calls would add
+        # their own host cost to every call of the small products)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            call(A, B, C)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wall_ms = (t1 - t0) * 1e3 / steps
+        kernel_ms = ev0.elapsed_time(ev1) / steps
+        # the spread of single calls, from as many more calls outside the timed region
+        per = per_call_events(steps)
     return {
         "workload": w, "A_host": A_h, "B_host": B_h, "A": A, "B": B, "C": C, "desc": desc, "variant": variant,
         "warmup_launches": warm,
-        "wall_ms": wall_ms, "kernel_ms": kernel_ms,
+        "wall_ms": wall_ms, "kernel_ms": kernel_ms, "kernel_ms_per_call": float(per.mean()),
         "kernel_ms_min": float(per.min()), "kernel_ms_median": float(np.median(per)),
         "kernel_ms_p90": float(np.percentile(per, 90)),
         "tflops_wall": w.flops / (wall_ms * 1e-3) / 1e12,
@@ -356,7 +380,6 @@ def mean_engine_clock(gpu_data):
 
 def vendor_blas(m, steps: int, warmup_seconds: float):
     """torch.matmul (fp32, TF32 off) on the same resident operands, timed like the product."""
-    import numpy as np
     import torch
 
     torch.backends.cuda.matmul.allow_tf32 = False
@@ -371,14 +394,15 @@ def vendor_blas(m, steps: int, warmup_seconds: float):
             torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
+    # as the product's timed region: the calls back to back between one pair of events
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
         torch.matmul(A, B, out=C)
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    ms = ev0.elapsed_time(ev1) / steps
     tflops = w.flops / (ms * 1e-3) / 1e12
     diff = float((C - m["C"]).abs().max().item())
     return {"what": "torch.matmul float32, TF32 off (ROCm BLAS); context, not a target",
@@ -787,8 +811,9 @@ def main():
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
-        "kernel_ms": {"mean": round(m["kernel_ms"], 4), "min": round(m["kernel_ms_min"], 4),
-                      "median": round(m["kernel_ms_median"], 4), "p90": round(m["kernel_ms_p90"], 4)},
+        "kernel_ms": {"mean": round(m["kernel_ms"], 4), "per_call_mean": round(m["kernel_ms_per_call"], 4),
+                      "min": round(m["kernel_ms_min"], 4), "median": round(m["kernel_ms_median"], 4),
+                      "p90": round(m["kernel_ms_p90"], 4)},
         "algorithmic_hbm_gbs": round(w.algorithmic_bytes / (m["kernel_ms"] * 1e-3) / 1e9, 1),
         "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
                    "hip": torch.version.hip},
@@ -823,6 +848,7 @@ def main():
             "steps": steps,
             "pct_of_fp32_matrix_peak": round(100.0 * ma["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2),
             "kernel_ms_mean": round(ma["kernel_ms"], 5),
+            "kernel_ms_per_call_mean": round(ma["kernel_ms_per_call"], 5),
             "kernel_ms_median": round(ma["kernel_ms_median"], 5),
             "roofline_frac": round(ma["tflops_kernel"] / PEAK_FP32_MATRIX_TFLOPS, 4),
             "algorithmic_hbm_gbs": round(wa.algorithmic_bytes / (ma["kernel_ms"] * 1e-3) / 1e9, 1),
