@@ -206,7 +206,8 @@ def test_variant_choice(lib):
     assert chosen(4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
     assert chosen(16384, 5000, 8192) == "m256n256k16_w2x2_vec4"   # 8.96 ms against 9.03
     assert chosen(8192, 4096, 1024) == "m256n128k16_w2x2_vec4"    # 472 µs against 477
-    # ragged: three rounds of 160×128 tiles, 223.5 µs against 234.6 for one of 256×128
+    # ragged: 760 tiles of 160×128, three per CU at most, 219-222 µs against 234 for the
+    # 480 tiles of 256×128 in one round
     assert chosen(3000, 5000, 1000) == "m160n128k32_w1x4_vec4_nn"
     # that tile stores C four columns at a time: not chosen when C's rows are
     # not 16-byte aligned (it would store one element at a time)
