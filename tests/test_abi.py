@@ -236,6 +236,25 @@ def test_variant_choice(lib):
     assert tg.tgemm_sgemm_variant_for(4, 4, 4, A_, 2, B_, 4, C_, 4) == -1  # lda < K
 
 
+def test_row_store_configuration_needs_aligned_c(lib):
+    """The 160×128 configuration writes C in 16-byte row pieces: over a grid
+    of shapes, the automatic choice takes it only when C and ldc are 16-byte
+    aligned, and takes some other configuration (not none) otherwise."""
+    names = tg.variant_names()
+    row_store = names.index("m160n128k32_w1x4_vec4_nn")
+    picked_aligned = 0
+    for M in (1000, 2560, 3000, 5000):
+        for N in (1000, 2048, 5000):
+            for K in (1000, 4096):
+                a, b, c = 1 << 40, 1 << 44, 1 << 46
+                v = tg.tgemm_sgemm_variant_for(M, N, K, a, K, b, N, c, N)
+                picked_aligned += v == row_store
+                for c_off, ldc in ((4, N), (0, N + 1), (8, N + 2)):
+                    w = tg.tgemm_sgemm_variant_for(M, N, K, a, K, b, N, c + c_off, ldc)
+                    assert w >= 0 and w != row_store, (M, N, K, c_off, ldc)
+    assert picked_aligned > 0
+
+
 def test_header_enums_match_binding():
     text = open(HEADER).read()
     for name in ("TGEMM_OP_N", "TGEMM_OP_T", "TGEMM_TRANSPOSE_BLOCKED", "TGEMM_TRANSPOSE_NAIVE",
