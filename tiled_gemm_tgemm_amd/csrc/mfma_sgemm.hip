@@ -684,25 +684,27 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 // Efficiencies measured on MI355X, as fractions of the matrix-core peak, with
 // one resident work-group per CU (alone) and with the CU full, plus a fixed
 // cost per round of work-groups (SIMD cycles); api.cpp adds the exposed store
-// of the last round.  Fitted to two sweeps of 76 shapes in all (64³ to
-// 16384×6144×8192: square, ragged, skinny, long and short K) timing every
-// configuration: the model's pick is the measured fastest or within 1.0% of
-// it on every one.  The one-wavefront-per-SIMD 256×256 tile runs level with
-// 256×128 (8192³: 7.16-7.20 ms against 7.18-7.19) while moving 24% fewer
-// bytes (3.49 against 4.57 GB a launch), pulls ahead as K grows (16384×5000×8192:
-// 8.96 against 9.03 ms) and falls behind at short K (8192×4096×1024: 477
-// against 472 µs), which its higher fixed cost per round expresses: one
-// work-group per CU leaves its pipeline fill uncovered.  256×128 with A
-// transposed keeps one register set of staged loads (two spill) and runs
-// 3% slower than as stored (tn 0.969: 148.2 against 153.0 TFLOP/s at 8192³),
-// so Aᵀ·B goes to the 256×256 tile (153.0).  The 160×128 tile spreads
-// 3000×1000×5000 over three rounds of tiles instead of one of 256×128 tiles
-// (at most three of 160×128 per CU: 60 blocks of 32×32 against 64) and
-// leaves 248 tiles' stores exposed at the end instead of 480: 223.5 against
-// 234.6 µs.  Its phases hold 32 values of k (79 KB of LDS, still two
-// work-groups per CU): with 16 a phase is 2560 matrix-core cycles per
-// wavefront, and the tile sustained 0.88 alone and 0.92 full against 0.93
-// and 0.95 now (C4 228 µs).  The 4-byte-load
+// of the last round.  Fitted to sweeps of 73 shapes (64³ to 16384×6144×8192:
+// square, ragged, skinny, long and short K) timing every configuration, on
+// two boxes: the model's pick is the measured fastest or within 1.5% of it on
+// every one (mean 0.1%).  The one-wavefront-per-SIMD 256×256 tile runs level
+// with 256×128 on some boxes (8192³: 7.16-7.20 ms against 7.18-7.19) and
+// ahead on others (7.21 against 7.39 ms, where 256×128 runs at a lower clock)
+// while moving 24% fewer bytes (3.49 against 4.57 GB a launch); it pulls
+// ahead as K grows (16384×5000×8192: 8.96 against 9.03 ms) and falls behind
+// at short K (8192×4096×1024: 477 against 472 µs), which its higher fixed
+// cost per round expresses: one work-group per CU leaves its pipeline fill
+// uncovered.  256×128 with A transposed keeps one register set of staged
+// loads (two spill) and runs 3% slower than as stored (tn 0.969: 148.2
+// against 153.0 TFLOP/s at 8192³), so Aᵀ·B goes to the 256×256 tile (153.0).
+// The 160×128 tile spreads 3000×1000×5000 over 760 tiles, at most three per
+// CU (60 blocks of 32×32 against 64 with 256×128 tiles), and leaves 248
+// tiles' stores exposed at the end instead of 480: 219-222 against 234 µs.
+// Its phases hold 32 values of k (79 KB of LDS, still two work-groups per
+// CU): with 16 a phase is 2560 matrix-core cycles per wavefront and the tile
+// ran 228 µs there.  The 64×64 tile's full-CU rate, 0.88, is lower than its
+// best shapes alone would give: 3000³ runs in 437 µs on 64×64 tiles and 421
+// on 160×128.  The 4-byte-load
 // flavours keep their measured ratio to the 16-byte ones; the 32×32
 // K-split configurations were fitted to a sweep of 27 small, ragged, skinny
 // and long-K shapes with both load widths (one work-group per CU: 256 tiles
@@ -712,8 +714,8 @@ const MfmaVariant kVariants[] = {
     TGEMM_VARIANT_TN("m256n128k16_w2x2_vec4", Large4, 0.975, 0.977, 7000.0, 0.969),
     TGEMM_VARIANT("m256n256k16_w2x2_vec4", Huge4, 0.979, 0.979, 13000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.965, 0.965, 7000.0),
-    TGEMM_VARIANT("m160n128k32_w1x4_vec4_nn", Wide4, 0.93, 0.95, 14000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.93, 7000.0),
+    TGEMM_VARIANT("m160n128k32_w1x4_vec4_nn", Wide4, 0.93, 0.97, 4000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.88, 7000.0),
     TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.937, 0.957, 7000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.844, 0.895, 7000.0),
     TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.69, 0.879, 7000.0),
