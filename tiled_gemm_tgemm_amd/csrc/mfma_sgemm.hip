@@ -454,15 +454,19 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
             }
         };
 
+        // phases 0 .. NS-1 are in flight before phase 0 is written, so that
+        // the first phases' memory latencies overlap (the set holding phase 0
+        // takes phase NS once it is written).  Phases past the last one are
+        // loaded too (a buffer extent that ends inside the operand's valid
+        // rows or is empty, and never written to LDS): with the loads
+        // unconditional the compiler's count of loads in flight at the loop
+        // head is exact, and each LDS write waits for its own phase's loads
+        // only
         issue(G::NS - 1, 0, cut(0));
-        store(G::NS - 1, 0);
-        // phases past the last one are loaded too (a buffer extent that ends
-        // inside the operand's valid rows or is empty, and never written to
-        // LDS): with the loads unconditional the compiler's count of loads
-        // in flight at the loop head is exact, and each LDS write waits for
-        // its own phase's loads only
 #pragma unroll
-        for (int s = 0; s < G::NS; ++s) issue(s, s + 1, cut(s + 1));
+        for (int s = 0; s + 1 < G::NS; ++s) issue(s, s + 1, cut(s + 1));
+        store(G::NS - 1, 0);
+        issue(G::NS - 1, G::NS, cut(G::NS));
         __syncthreads();
         rd(f[0], 0, 0);
         int p = 0;
