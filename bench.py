@@ -274,6 +274,18 @@ def time_workload(w, kernel: str, steps: int, warmup: int, warmup_seconds: float
         # a 512 MiB fill before every call; the wall clock would cover the
         # fills too, so the figure is the calls' own event time
         flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        # the first fill of a new buffer maps its pages (~5 ms) and the calls
+        # after it run up to 20% slow for ~15 ms: the flush-and-call loop is
+        # warmed up as the plain calls were before it is timed
+        i = 0
+        t_cold = time.perf_counter()
+        while i < warmup or time.perf_counter() - t_cold < warmup_seconds:
+            flush.fill_(float(i))
+            call(A, B, C)
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
         per = per_call_events(steps, flush)
         wall_ms = kernel_ms = float(per.mean())
     else:
