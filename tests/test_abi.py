@@ -152,10 +152,10 @@ def test_transposed_variant_choice(lib):
     # Aᵀ·B goes to the one-wavefront-per-SIMD 256×256 tile, which keeps two
     # register sets of staged loads (MI355X, 8192³: 153.0 against 148.2
     # TFLOP/s for 256×128; 4096³: 151.4 against 146.5)
-    assert chosen(T_, N_, 4096, 4096, 4096, 4096, 4096) == "m256n256k16_w2x2_vec4"
-    assert chosen(T_, N_, 8192, 8192, 8192, 8192, 8192) == "m256n256k16_w2x2_vec4"
+    assert chosen(T_, N_, 4096, 4096, 4096, 4096, 4096) == "m256n256k16_w2x4_vec4"
+    assert chosen(T_, N_, 8192, 8192, 8192, 8192, 8192) == "m256n256k16_w2x4_vec4"
     assert chosen(N_, T_, 4096, 4096, 4096, 4096, 4096) == "m256n128k16_w2x2_vec4"   # 151.7 against 150.8
-    assert chosen(N_, T_, 8192, 8192, 8192, 8192, 8192) == "m256n256k16_w2x2_vec4"
+    assert chosen(N_, T_, 8192, 8192, 8192, 8192, 8192) == "m256n256k16_w2x4_vec4"
     assert chosen(T_, T_, 512, 512, 512, 512, 512) == "m32n32k32_w1x1s8_vec4"
     # Aᵀ with M not a multiple of 4: its stored rows cannot take 16-byte loads
     assert chosen(T_, N_, 4098, 4096, 4096, 4098, 4096).endswith("vec1")
@@ -202,9 +202,9 @@ def test_variant_choice(lib):
 
     # MI355X: 8192³ 7.16-7.20 ms (256×256) against 7.18-7.19 (256×128) with 24%
     # fewer bytes moved; 4096³ 905-909 µs (256×128) against 908-912 (256×256)
-    assert chosen(8192, 8192, 8192) == "m256n256k16_w2x2_vec4"
+    assert chosen(8192, 8192, 8192) == "m256n256k16_w2x4_vec4"
     assert chosen(4096, 4096, 4096) == "m256n128k16_w2x2_vec4"
-    assert chosen(16384, 5000, 8192) == "m256n256k16_w2x2_vec4"   # 8.96 ms against 9.03
+    assert chosen(16384, 5000, 8192) == "m256n256k16_w2x4_vec4"   # 8.96 ms against 9.03
     assert chosen(8192, 4096, 1024) == "m256n128k16_w2x2_vec4"    # 472 µs against 477
     # ragged: 760 tiles of 160×128, three per CU at most, 219-222 µs against 234 for the
     # 480 tiles of 256×128 in one round

@@ -653,8 +653,11 @@ constexpr int64_t max_ldb_t()
 
 //             BM   BN  BK VEC GROUP_M OCC
 typedef Shape<256, 128, 16, 4, 4, 2, 1, 2, 2, 1> Large4;  // Aᵀ·B: one register set (two spill)
-// one wavefront per SIMD holding a 128×128 sub-tile (512 registers)
-typedef Shape<256, 256, 16, 4, 4, 1> Huge4;
+// one work-group per CU: eight wavefronts, two per SIMD, each holding a
+// 128×64 sub-tile (256 registers).  The same tile as four wavefronts of
+// 128×128, one per SIMD with 256 accumulators in AGPRs, ran 0.1-1.7% slower
+// (mean 0.35%) on 27 shape and operand-order cases, bit-identical
+typedef Shape<256, 256, 16, 4, 4, 2, 1, 2, 2, 2, 4> Huge4;
 typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
 // 160 rows of A as stored (5 passes of 32 at 32 values of k); four wavefronts
 // side by side, each 160×32.  Its blocks are formed transposed (operands
@@ -662,7 +665,7 @@ typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
 // of C and the epilogue writes 16-byte pieces of rows: 3000×1000×5000 in
 // 219.3 against 223.7 µs with the column-wise epilogue, bit-identical (the
 // same exchange costs 0.6-0.9% on 128×128 tiles at 2048³, and 256×256
-// tiles, whose accumulators live in AGPRs, spill with it)
+// tiles spilled with it)
 typedef Shape<160, 128, 32, 4, 4, 2, 1, 2, 1, 2, 4, false, true> Wide4;
 typedef Shape<64, 64, 32, 4, 8, 4> Small4;
 typedef Shape<256, 128, 16, 1, 4, 2, 1, 1> Large1;  // one register set (two spill)
@@ -691,7 +694,7 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 // of the last round.  Fitted to sweeps of 73 shapes (64³ to 16384×6144×8192:
 // square, ragged, skinny, long and short K) timing every configuration, on
 // two boxes: the model's pick is the measured fastest or within 1.5% of it on
-// every one (mean 0.1%).  The one-wavefront-per-SIMD 256×256 tile runs level
+// every one (mean 0.1%).  The one-work-group-per-CU 256×256 tile runs level
 // with 256×128 on some boxes (8192³: 7.16-7.20 ms against 7.18-7.19) and
 // ahead on others (7.21 against 7.39 ms, where 256×128 runs at a lower clock)
 // while moving 24% fewer bytes (3.49 against 4.57 GB a launch); it pulls
@@ -716,7 +719,7 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 // from 256³ and 512³).
 const MfmaVariant kVariants[] = {
     TGEMM_VARIANT_TN("m256n128k16_w2x2_vec4", Large4, 0.975, 0.977, 7000.0, 0.969),
-    TGEMM_VARIANT("m256n256k16_w2x2_vec4", Huge4, 0.979, 0.979, 13000.0),
+    TGEMM_VARIANT("m256n256k16_w2x4_vec4", Huge4, 0.979, 0.979, 13000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.965, 0.965, 7000.0),
     TGEMM_VARIANT("m160n128k32_w1x4_vec4_nn", Wide4, 0.93, 0.97, 4000.0),
     TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.88, 7000.0),
