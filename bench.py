@@ -473,6 +473,19 @@ def transpose_traffic_for(workload_name: str, kernel: str):
     return entry.get("hbm_bytes_per_launch") if entry else None
 
 
+def cpu_model(path: str = "/proc/cpuinfo"):
+    """The host CPU's model name from /proc/cpuinfo (None where it has none)."""
+    try:
+        with open(path) as f:
+            for text in f:
+                key, sep, value = text.partition(":")
+                if sep and key.strip() == "model name":
+                    return value.strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(m, target_s: float, others=(), one_thread_workload=None):
     """The oracle (float64 sums of exact float32 products, plus the sums of
     |products|) timed on this host's cores.  `value`: whole rows of the
@@ -503,7 +516,7 @@ def cpu_baseline(m, target_s: float, others=(), one_thread_workload=None):
     C_rows = m["C"][:rows].cpu().numpy().astype(np.float64)
     out = {
         "value": 2.0 * macs / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-        "kind": "oracle",
+        "kind": "oracle", "cpu": cpu_model(), "cpus_allowed": len(os.sched_getaffinity(0)),
         "sample": f"first {rows} rows of C ({rows}x{w.N}, K={w.K}) of {w.name}: float64 sums "
                   f"with exact float32 products, plus the sums of |products|; {t:.2f} s",
         "sample_rows_within_bound": bool(np.all(np.abs(C_rows - P) <= 4.0 * w.K * 2.0 ** -24 * S)),

@@ -120,3 +120,13 @@ def test_step_counts_per_workload():
     assert bench.steps_for(W["rect3000x1000x5000_normal"], A) == 50
     assert bench.steps_for(W["square4096_uniform"], A) == 20
     assert bench.steps_for(W["square8192_uniform"], A) == 20
+
+
+def test_cpu_model_is_read_from_cpuinfo(tmp_path):
+    info = tmp_path / "cpuinfo"
+    info.write_text("processor\t: 0\nvendor_id\t: AuthenticAMD\nmodel name\t: AMD EPYC 9575F 64-Core Processor\n"
+                    "processor\t: 1\nmodel name\t: AMD EPYC 9575F 64-Core Processor\n")
+    assert bench.cpu_model(str(info)) == "AMD EPYC 9575F 64-Core Processor"
+    info.write_text("processor\t: 0\nfeatures\t: fp asimd\n")
+    assert bench.cpu_model(str(info)) is None
+    assert bench.cpu_model(str(tmp_path / "missing")) is None
