@@ -191,3 +191,62 @@ def test_layout_sweep_splitk_integer_exact(case):
     got, rest = sc.window()
     assert np.array_equal(got.astype(np.float64), want), f"case {i}: split-K result differs"
     assert np.all(rest == SENTINEL), f"case {i}: split-K wrote C outside its window"
+
+
+def scaled_inputs(M, N, K, seed):
+    """Real inputs over a wide range: N(0,1) values with each row of A and
+    each column of B scaled by 2^e, e uniform in [-12, 12] (exact in float32,
+    no subnormal products), and for every third seed the second half of A's
+    columns equal to the first half and the second half of B's rows the
+    negated first half perturbed by about 2^-10, so that the sums cancel and
+    C is about 2^-10 of S."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K)) * np.exp2(rng.integers(-12, 13, (M, 1)))
+    B = rng.standard_normal((K, N)) * np.exp2(rng.integers(-12, 13, (1, N)))
+    if seed % 3 == 0 and K >= 2:
+        h = K // 2
+        A[:, h:2 * h] = A[:, :h]
+        B[h:2 * h] = -B[:h] * (1.0 + np.exp2(-10) * rng.uniform(-1.0, 1.0, (h, N)))
+    return A.astype(np.float32), B.astype(np.float32)
+
+
+@pytest.mark.parametrize("case", draw_cases()[:20], ids=lambda c: f"c{c[0]}_{c[1]}x{c[2]}x{c[3]}")
+def test_layout_sweep_real_within_bound(case):
+    i, M, N, K, ta, tb, pads, offs = case
+    log(f"layout real case {i}: M={M} N={N} K={K} ta={ta} tb={tb} pads={pads} offsets={offs}")
+    A, B = scaled_inputs(M, N, K, 300 + i)
+    P, S = oracle.gemm(A, B)
+    bound = 4.0 * K * 2.0 ** -24 * S
+    fma = oracle.gemm_fma_f32(A, B) if not (ta or tb) else None
+    sa = Stored(A.T if ta else A, offs[0], pads[0], np.nan)
+    sb = Stored(B.T if tb else B, offs[1], pads[1], np.nan)
+    op_a = tg.TGEMM_OP_T if ta else tg.TGEMM_OP_N
+    op_b = tg.TGEMM_OP_T if tb else tg.TGEMM_OP_N
+    stream = torch.cuda.current_stream().cuda_stream
+    ran = 0
+    worst = 0.0
+    for label, call in entry_points(M, N, K, ta, tb):
+        sc = Stored(np.zeros((M, N), np.float32), offs[2], pads[2], SENTINEL)
+        sc.buf.fill_(float(SENTINEL))
+        st = call(op_a, op_b, sa.ptr, sa.ld, sb.ptr, sb.ld, sc.ptr, sc.ld, stream)
+        if st == tg.TGEMM_ERROR_NOT_SUPPORTED and label != "auto":
+            continue
+        assert st == tg.TGEMM_SUCCESS, f"{label}: status {tg.tgemm_status_string(st)}"
+        torch.cuda.synchronize()
+        got, rest = sc.window()
+        assert np.all(np.isfinite(got)), f"case {i} {label}: non-finite output"
+        err = np.abs(got.astype(np.float64) - P)
+        bad = err > bound
+        if bad.any():
+            r, c = np.argwhere(bad)[0]
+            pytest.fail(f"case {i} {label}: {bad.sum()} elements outside the bound; first ({r},{c}) "
+                        f"C={got[r, c]!r} P={P[r, c]!r} bound={bound[r, c]!r}")
+        if label in ("naive", "lds16p1", "lds32p0", "simt"):
+            # one fused multiply-add per k in ascending order: the oracle's float32 model bit for bit
+            assert np.array_equal(got.view(np.uint32), fma.view(np.uint32)), f"case {i} {label}: differs from the FMA chain"
+        assert np.all(rest == SENTINEL), f"case {i} {label}: C written outside its window"
+        pos = S > 0
+        if pos.any():
+            worst = max(worst, float((err[pos] / (K * 2.0 ** -24 * S[pos])).max()))
+        ran += 1
+    log(f"  within the bound through {ran} entry points; worst ratio {worst:.4f} of K·2^-24·S")
