@@ -92,7 +92,7 @@
 //   [s·kchunk, min(K, (s+1)·kchunk)) and writes its partial tiles to block s
 //   of a workspace; splitk_sum.hip adds the blocks in slice order.  The grid
 //   is then one work-group per tile and slice.
-// * "More work per thread" (page 1, end of "Tile Size 결정"): each 64-lane
+// * More work per thread (page 1, end of "Tile Size 결정"): each 64-lane
 //   wavefront owns a (BM/WM)×(BN/WN) sub-tile held in accumulator registers
 //   for the whole K loop, built from 32×32 blocks of v_mfma_f32_32x32x2_f32.
 //   C is written once at the end: by columns (a lane's accumulators are four
