@@ -785,3 +785,44 @@ def test_concurrent_products_on_two_streams():
         for rep in range(3):
             log(f"concurrent stream {i} call {rep}")
             assert_exact(outs[i][rep].cpu().numpy(), want[i], f"stream {i} call {rep}")
+
+
+def test_side_stream_output_allocation_waits_for_current_stream():
+    """sgemm and transpose with `out` omitted and a side stream given: the
+    output is allocated on the current stream, whose pending work may still
+    read the block's previous owner.  Here a tensor X is freed while a copy
+    of it, queued behind several milliseconds of other work, is still
+    pending on the current stream; the output allocated next (same size) may
+    be handed X's block.  The binding makes the side stream wait for the
+    current one first, so the copy still sees X and the product is exact."""
+    M, N, K = 1024, 1024, 512
+    A, B = int_inputs(M, N, K, 91)
+    Pi = oracle.gemm_i64(A, B)
+    dA, dB = dev(A), dev(B)
+    T = np.arange(M * N, dtype=np.float32).reshape(M, N)  # exact in float32
+    dT = dev(T)
+    side = torch.cuda.Stream()
+    W = torch.rand(4096, 4096, device="cuda")
+    V = torch.empty_like(W)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        log(f"side-stream allocation, rep {rep}")
+        for what in ("sgemm", "transpose"):
+            X = torch.full((M, N), 1.5, device="cuda")
+            Z = torch.empty_like(X)
+            for _ in range(3):
+                tg.sgemm(W, W, out=V)  # several ms of work on the current stream
+            Z.copy_(X)                 # reads X once that work is done
+            del X                      # X's block goes back to the cache, still to be read
+            if what == "sgemm":
+                C = tg.sgemm(dA, dB, stream=side.cuda_stream)
+            else:
+                C = tg.transpose(dT, stream=side.cuda_stream)  # N×M output: the size of X
+            side.synchronize()
+            torch.cuda.synchronize()
+            assert bool(torch.all(Z == 1.5)), f"{what} rep {rep}: the side stream wrote X's block before it was read"
+            if what == "sgemm":
+                assert_exact(C.cpu().numpy(), Pi, f"side-stream sgemm rep {rep}")
+            else:
+                assert np.array_equal(C.cpu().numpy(), T.T), f"side-stream transpose rep {rep}"
+            del C, Z

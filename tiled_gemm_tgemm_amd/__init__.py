@@ -75,16 +75,21 @@ def _layout(t, name):
 
 def _hold_for_stream(stream, device, *tensors):
     """Tensors allocated here (on torch's current stream) but used by work
-    queued on another `stream`: record that stream on them, so that torch's
-    caching allocator does not hand their memory out again, once they are
+    queued on another `stream`.  Torch's caching allocator orders a block's
+    reuse on the stream it was allocated on only, so: `stream` first waits for
+    the work already queued on the current stream (a block just handed out
+    may still be in use there by its previous owner), and the tensors record
+    `stream`, so that their memory is not handed out again, once they are
     released, before the work queued on `stream` so far has finished."""
     import torch
 
     if stream is None or not tensors:
         return
-    if int(stream) == int(torch.cuda.current_stream(device).cuda_stream):
+    current = torch.cuda.current_stream(device)
+    if int(stream) == int(current.cuda_stream):
         return
     other = torch.cuda.ExternalStream(stream, device=device)
+    other.wait_stream(current)
     for t in tensors:
         t.record_stream(other)
 
@@ -241,8 +246,10 @@ def transpose(A, out=None, *, kernel="blocked", stream=None):
     M, N = A.shape
     if A.stride(1) != 1 and N > 1:
         raise ValueError("A must be row-major")
+    made = []
     if out is None:
         out = torch.empty((N, M), dtype=torch.float32, device=A.device)
+        made.append(out)
     else:
         out = _check(out, "out")
         if tuple(out.shape) != (N, M):
@@ -253,6 +260,7 @@ def transpose(A, out=None, *, kernel="blocked", stream=None):
         raise ValueError(f"kernel must be one of {tuple(TRANSPOSE_KERNELS)}")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
+    _hold_for_stream(stream, A.device, *made)
     st = tgemm_transpose(M, N, A.data_ptr(), max(A.stride(0), N, 1), out.data_ptr(), max(out.stride(0), M, 1),
                          TRANSPOSE_KERNELS[kernel], stream)
     if st != TGEMM_SUCCESS:
