@@ -58,7 +58,9 @@
 //   pointing every work-group at one cached tile gains 0.3%.
 // * Within a phase the memory work is interleaved with the MFMAs: each
 //   k-group's MFMAs cover the reads of the next group's fragments; the
-//   first group's also cover the write of phase p+1; the barrier sits before
+//   first group's also cover the write of phase p+1 (where a group has too
+//   few MFMAs for that, the 64×64 tile, A's part of the write goes with the
+//   first group and B's with the second); the barrier sits before
 //   the last k-group, whose fragments are already in registers, so the last
 //   group's MFMAs cover the reads of phase p+1's first fragments and the
 //   loads.  Every LDS access then has a k-group of MFMAs to complete in.
@@ -238,7 +240,7 @@ struct Loader {
 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int VEC_, int GROUP_M_, int OCC_, bool TA_,
-          bool TB_, int KS_ = 1, int NS_ = 2, bool SWAPC_ = false>
+          bool TB_, int KS_ = 1, int NS_ = 2, bool SWAPC_ = false, bool WSPLIT_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, VEC = VEC_;
     static constexpr int KS = KS_;                     // K slices per work-group (see the kernel)
@@ -248,6 +250,7 @@ struct Cfg {
     static_assert(NS == 1 || NS == 2, "one or two register sets");
     static constexpr bool TA = TA_, TB = TB_;          // operands stored transposed
     static constexpr bool SWAPC = SWAPC_ && KS_ == 1;  // blocks formed transposed, C stored by rows
+    static constexpr bool WSPLIT = WSPLIT_ && BK_ >= 24;  // A's LDS writes in k-group 0, B's in k-group 1
     static constexpr int NTS = kWave * WM * WN;        // threads per K slice
     static constexpr int NT = NTS * KS;                // threads per work-group
     static constexpr int TM = BM / WM, TN = BN / WN;   // wavefront sub-tile
@@ -388,6 +391,8 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
             la[s].store(st);
             lb[s].store(st + G::A_STAGE);
         };
+        auto store_a = [&] __device__(int s, int r) { la[s].store(slds + (r & 1) * G::STAGE); };
+        auto store_b = [&] __device__(int s, int r) { lb[s].store(slds + (r & 1) * G::STAGE + G::A_STAGE); };
 
         typedef mfma::Fragments<G::FM, G::FN, LA::KC, LA::S, LB::KC, LB::S> Frag;
         constexpr int NG = G::BK / 8;                                             // k-groups per phase
@@ -422,7 +427,9 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
             };
             // k-group g's MFMAs run while group g+1's fragments are read (f[0]
             // holds group 0 on entry); the first group's MFMAs also cover the
-            // writes of phase r+1 into the other stage.  The one barrier comes
+            // writes of phase r+1 into the other stage (with WSPLIT, A's part;
+            // B's goes with the second group, so that a group of few MFMAs
+            // does not issue the whole write in one burst).  The one barrier comes
             // before the last group, whose fragments are already in registers:
             // it certifies that stage r+1 is complete and that stage r is read
             // no more, so the last group's MFMAs cover the reads of phase r+1's
@@ -435,10 +442,17 @@ void mfma_sgemm_kernel(int M, int N, int K, const float *__restrict__ A, int64_t
             for (int g = 0; g < NG; ++g) {
                 if (g + 1 < NG) {
                     rd(f[(g + 1) & 1], r & 1, g + 1);
-                    if (g == 0 && next) store(s, r + 1);
+                    if constexpr (G::WSPLIT) {
+                        if (g == 0 && next) store_a(s, r + 1);
+                        if (g == 1 && next) store_b(s, r + 1);
+                    } else {
+                        if (g == 0 && next) store(s, r + 1);
+                    }
                     if (g < ng) mgroup(acc, f[g & 1]);
                     if (g == 0)
-                        mfma::interleave<NM, RD, 0x100, WR, 0x200, 0>();
+                        mfma::interleave<NM, RD, 0x100, G::WSPLIT ? LA::L : WR, 0x200, 0>();
+                    else if (G::WSPLIT && g == 1)
+                        mfma::interleave<NM, RD, 0x100, LB::L, 0x200, 1>();
                     else
                         mfma::interleave<NM, RD, 0x100, 0, 0x200, 1>();
                 } else {
@@ -610,10 +624,10 @@ constexpr int64_t max_ld()
 // the most LDS addresses live.  TRANS: the shape also runs transposed
 // operands (a transposed slice must split into whole rows per pass too).
 template <int BM, int BN, int BK, int VEC, int GM, int OCC, int KS = 1, int NS = 2, int W = 2, int NS_TN = NS,
-          int WN = W, bool TRANS = true, bool SWAPC = false>
+          int WN = W, bool TRANS = true, bool SWAPC = false, bool WSPLIT = false>
 struct Shape {
     template <bool TA, bool TB>
-    using C = Cfg<BM, BN, BK, W, WN, VEC, GM, OCC, TA, TB, KS, (TA && !TB) ? NS_TN : NS, SWAPC>;
+    using C = Cfg<BM, BN, BK, W, WN, VEC, GM, OCC, TA, TB, KS, (TA && !TB) ? NS_TN : NS, SWAPC, WSPLIT>;
     static constexpr bool trans = TRANS;
     static constexpr bool c16 = SWAPC;
     static hipError_t launch(const GemmArgs &g, hipStream_t stream)
@@ -667,10 +681,18 @@ typedef Shape<128, 128, 32, 4, 8, 2> Mid4;
 // same exchange costs 0.6-0.9% on 128×128 tiles at 2048³, and 256×256
 // tiles spilled with it)
 typedef Shape<160, 128, 32, 4, 4, 2, 1, 2, 1, 2, 4, false, true> Wide4;
-typedef Shape<64, 64, 32, 4, 8, 4> Small4;
+// 64×64: one 32×32 block per wavefront, so a k-group is only four MFMAs and
+// cannot cover the phase's four LDS writes next to its three fragment reads.
+// Written in one burst after the first group, the writes filled the LDS data
+// queue and the wavefronts then waited to issue their next LDS reads (at
+// 1024³, 7.1e5 wave-cycles of SQ_WAIT_INST_LDS and 2.7e5 cycles of
+// SQ_LDS_DATA_FIFO_FULL against 1.1e5 and 2.5e4 for the vendor BLAS kernel of
+// the same tile); A's writes after group 0 and B's after group 1 took 1024³
+// from 20.3 to 19.2 µs and 1024×1024×8192 from 131.4 to 123.2, bit-identical
+typedef Shape<64, 64, 32, 4, 8, 4, 1, 2, 2, 2, 2, true, false, true> Small4;
 typedef Shape<256, 128, 16, 1, 4, 2, 1, 1> Large1;  // one register set (two spill)
 typedef Shape<128, 128, 32, 1, 8, 2> Mid1;
-typedef Shape<64, 64, 32, 1, 8, 4> Small1;
+typedef Shape<64, 64, 32, 1, 8, 4, 1, 2, 2, 2, 2, true, false, true> Small1;
 typedef Shape<32, 32, 32, 4, 8, 2, 4, 2, 1> Tiny4x4;  // one wavefront per K slice
 typedef Shape<32, 32, 32, 4, 8, 2, 8, 2, 1> Tiny4x8;
 typedef Shape<32, 32, 32, 1, 8, 2, 4, 2, 1> Tiny1x4;
@@ -709,9 +731,11 @@ typedef Shape<32, 32, 32, 1, 8, 2, 8, 2, 1> Tiny1x8;
 // tiles' stores exposed at the end instead of 480: 219-222 against 234 µs.
 // Its phases hold 32 values of k (79 KB of LDS, still two work-groups per
 // CU): with 16 a phase is 2560 matrix-core cycles per wavefront and the tile
-// ran 228 µs there.  The 64×64 tile's full-CU rate, 0.88, is lower than its
-// best shapes alone would give: 3000³ runs in 437 µs on 64×64 tiles and 421
-// on 160×128.  The 4-byte-load
+// ran 228 µs there.  The 64×64 entries were refitted after its LDS writes
+// were split over two k-groups, together with the split-K counts, on a sweep
+// of 36 shapes with both load widths: 3000³ now runs in 409 µs on 64×64
+// tiles against 421 on 160×128, and small products with unaligned operands
+// go to the 32×32 K split.  The 4-byte-load
 // flavours keep their measured ratio to the 16-byte ones; the 32×32
 // K-split configurations were fitted to a sweep of 27 small, ragged, skinny
 // and long-K shapes with both load widths (one work-group per CU: 256 tiles
@@ -722,10 +746,10 @@ const MfmaVariant kVariants[] = {
     TGEMM_VARIANT("m256n256k16_w2x4_vec4", Huge4, 0.979, 0.979, 13000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec4", Mid4, 0.965, 0.965, 7000.0),
     TGEMM_VARIANT("m160n128k32_w1x4_vec4_nn", Wide4, 0.93, 0.97, 4000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.82, 0.88, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec4", Small4, 0.84, 0.88, 7000.0),
     TGEMM_VARIANT("m256n128k16_w2x2_vec1", Large1, 0.937, 0.957, 7000.0),
     TGEMM_VARIANT("m128n128k32_w2x2_vec1", Mid1, 0.844, 0.895, 7000.0),
-    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.69, 0.879, 7000.0),
+    TGEMM_VARIANT("m64n64k32_w2x2_vec1", Small1, 0.64, 0.87, 9000.0),
     TGEMM_VARIANT("m32n32k32_w1x1s4_vec4", Tiny4x4, 0.45, 0.61, 9500.0),
     TGEMM_VARIANT("m32n32k32_w1x1s8_vec4", Tiny4x8, 0.60, 0.60, 11500.0),
     TGEMM_VARIANT("m32n32k32_w1x1s4_vec1", Tiny1x4, 0.24, 0.37, 12000.0),
